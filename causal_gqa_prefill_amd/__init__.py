@@ -1,0 +1,16 @@
+"""Causal GQA prefill attention for AMD MI355X (gfx950).
+
+attn_prefill(q, k, v, scale=None, causal=True) -> (out, lse) runs the
+hand-written HIP kernels in libattn_prefill.so.  Importing the package loads
+nothing; the first use of the attention entry points loads the library and
+raises if it is missing (there is no CPU fallback).
+"""
+
+__all__ = ["attn_prefill", "attn_prefill_into", "library", "AttnPrefillError"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,59 @@
+"""The five attention-layer workloads this library is measured and tested on.
+
+Shapes: "flops / prefill-attention", section "Arithmetic intensity", names the
+Llama-2-7B (MHA), Llama-3-8B (GQA-4) and Llama-2-70B (GQA-8) attention
+geometries; "Long-Context Attention Explained" gives the made-up 36-query /
+6-key-value-head, 128-wide shape at 128K tokens.  Inputs are synthetic
+N(0, 1) bf16 tensors drawn from a seed (seed = 1000 + config index); no
+trained weights or activations are involved.
+"""
+from dataclasses import dataclass
+import math
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class AttnConfig:
+    index: int
+    name: str
+    B: int
+    L: int
+    n_q: int
+    n_kv: int
+    d_h: int
+    causal: bool = True
+    sampled_rows: int = 0  # 0: the oracle checks every row
+
+    @property
+    def g(self) -> int:
+        return self.n_q // self.n_kv
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(d_h) rounded to fp32, the value the library receives."""
+        return float(np.float32(1.0 / math.sqrt(self.d_h)))
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+    def describe(self) -> str:
+        return (f"{self.name}: B={self.B} L={self.L} n_q={self.n_q} "
+                f"n_kv={self.n_kv} d_h={self.d_h} causal={int(self.causal)}")
+
+
+CONFIGS = [
+    AttnConfig(1, "tiny causal MHA", 1, 128, 4, 4, 64),
+    AttnConfig(2, "Llama-2-7B-shaped MHA layer", 4, 2048, 32, 32, 128),
+    AttnConfig(3, "Llama-3-8B-shaped GQA-4 layer", 1, 8192, 32, 8, 128),
+    AttnConfig(4, "Llama-2-70B-shaped GQA-8 layer", 1, 32768, 64, 8, 128,
+               sampled_rows=4096),
+    AttnConfig(5, "synthetic wide GQA-6 long context", 1, 131072, 36, 6, 128,
+               sampled_rows=4096),
+]
+
+
+def config(index: int) -> AttnConfig:
+    """Config by its 1-based index."""
+    return CONFIGS[index - 1]

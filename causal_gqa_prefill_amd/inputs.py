@@ -1,0 +1,74 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module holds no attention arithmetic: it draws normal samples, encodes
+them as bf16 bit patterns (round to nearest even), and picks query rows to
+sample.  Both the HIP path and the CPU oracle receive exactly these bits.
+
+Recipe: numpy default_rng(seed) (PCG64) standard_normal in float32, drawn in
+the order Q, K, V from one stream, each element rounded to bf16 with
+round-to-nearest-even.
+"""
+import numpy as np
+
+
+def bf16_bits(x) -> np.ndarray:
+    """float32 array -> bf16 bit patterns (uint16), round to nearest even.
+
+    Finite inputs only (the generators never produce NaN or Inf)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float32 (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def make_qkv(B, L, n_q, n_kv, d_h, seed):
+    """Q [B,n_q,L,d_h], K and V [B,n_kv,L,d_h] as bf16 bits from N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for heads in (n_q, n_kv, n_kv):
+        x = rng.standard_normal((B, heads, L, d_h), dtype=np.float32)
+        out.append(bf16_bits(x))
+        del x
+    return tuple(out)
+
+
+def make_config_qkv(cfg):
+    return make_qkv(cfg.B, cfg.L, cfg.n_q, cfg.n_kv, cfg.d_h, cfg.seed)
+
+
+def sample_rows(B, n_q, L, n, seed, block_rows=128):
+    """n distinct flat row ids (b * n_q + h) * L + i.
+
+    Four rows are always included: the first and last query of head 0, the
+    last query of the last head, and the first row of the second q-block of
+    the middle head.  The rest are drawn uniformly without replacement from the
+    remaining rows with default_rng(seed + 7).  Returned sorted."""
+    total = B * n_q * L
+    if n >= total:
+        return np.arange(total, dtype=np.int64)
+    forced = [0, L - 1, (n_q - 1) * L + (L - 1),
+              (n_q // 2) * L + min(block_rows, L - 1)]
+    forced = sorted(set(forced))
+    rng = np.random.default_rng(seed + 7)
+    picked = set(forced)
+    need = n - len(picked)
+    while need > 0:
+        cand = rng.integers(0, total, size=2 * need + 16, dtype=np.int64)
+        for c in cand.tolist():
+            if c not in picked:
+                picked.add(c)
+                need -= 1
+                if need == 0:
+                    break
+    return np.array(sorted(picked), dtype=np.int64)
+
+
+def row_coords(rows, n_q, L):
+    """flat row ids -> (b, h, i) arrays."""
+    rows = np.asarray(rows, dtype=np.int64)
+    return rows // (n_q * L), (rows // L) % n_q, rows % L

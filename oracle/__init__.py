@@ -1,0 +1,100 @@
+"""fp64 CPU oracle for causal GQA prefill attention -- TEST INFRASTRUCTURE.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its binding) never
+imports, links or calls it, and it imports nothing from the product package.
+
+The arithmetic lives in attn_oracle.c (plain definition: materialise the score
+row, mask, subtract the max, exponentiate, normalise, multiply by V, emit the
+natural-log LSE).  This module only loads that library (building it with gcc
+on first use if it is missing) and marshals numpy arrays.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+OK, BAD_ARG, NO_MEMORY = 0, 1, 2
+
+
+def load_library(path):
+    """Load an oracle shared library and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    lib.oracle_attn_rows.restype = ctypes.c_int
+    lib.oracle_attn_rows.argtypes = [
+        u16p, u16p, u16p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+        ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+        ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+        ctypes.POINTER(ctypes.c_uint64), ctypes.c_int,
+    ]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_version.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _lib = load_library(_build.LIB)
+    return _lib
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle uses by default."""
+    return int(_load().oracle_max_threads())
+
+
+def _bits(a, shape, name):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError(f"{name}: expected bf16 bit patterns as uint16, got {a.dtype}")
+    if a.shape != shape:
+        raise ValueError(f"{name}: expected shape {shape}, got {a.shape}")
+    return a
+
+
+def attention_rows(q, k, v, scale, causal=True, rows=None, threads=0, lib=None):
+    """Oracle attention for selected query rows.
+
+    q: uint16 [B, n_q, L, d_h] bf16 bits; k, v: uint16 [B, n_kv, L, d_h].
+    scale: the fp32 scale applied to Q K^T (passed as float32).
+    rows: None for every row, else flat row ids (b * n_q + h) * L + i.
+    lib: a library from load_library() (default: the built oracle).
+    Returns (out [n_rows, d_h] float64, lse [n_rows] float64, flops int).
+    """
+    if q.ndim != 4 or k.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B, heads, L, d_h]")
+    B, n_q, L, d_h = q.shape
+    n_kv = k.shape[1]
+    q = _bits(q, (B, n_q, L, d_h), "q")
+    k = _bits(k, (B, n_kv, L, d_h), "k")
+    v = _bits(v, (B, n_kv, L, d_h), "v")
+    if rows is None:
+        n_rows = B * n_q * L
+        rows_p = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = int(rows.size)
+        rows_p = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    out = np.empty((n_rows, d_h), dtype=np.float64)
+    lse = np.empty((n_rows,), dtype=np.float64)
+    flops = ctypes.c_uint64(0)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = (lib or _load()).oracle_attn_rows(
+        q.ctypes.data_as(u16p), k.ctypes.data_as(u16p), v.ctypes.data_as(u16p),
+        B, L, n_q, n_kv, d_h, float(np.float32(scale)), int(causal),
+        rows_p, n_rows, out.ctypes.data_as(dp), lse.ctypes.data_as(dp),
+        ctypes.byref(flops), int(threads))
+    if rc != OK:
+        raise ValueError(f"oracle_attn_rows failed with code {rc}")
+    return out, lse, int(flops.value)

@@ -1,0 +1,389 @@
+"""Pins for the fp64 CPU oracle (no GPU needed).
+
+Each test checks the oracle against something other than itself: 50-digit
+brute force, closed forms, invariants, a library routine (torch SDPA on the
+CPU in fp64), an independent tiled online-softmax written here from the
+pages' five steps, and numbers the pages print.  Together they are chosen so
+that a plausible slip in the oracle (a dropped max subtraction, a wrong mask
+boundary, a wrong key/value head, a wrong log base, a transposed operand, a
+mis-applied scale) fails at least one of them; test_oracle_mutants.py checks
+exactly that.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from causal_gqa_prefill_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_numbers.json")
+
+
+def _bits_from_f32(x):
+    return inputs.bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def _vals(bits):
+    return inputs.bf16_to_f32(bits).astype(np.float64)
+
+
+def _random_case(B, L, n_q, n_kv, d, seed, mult=1.0):
+    q, k, v = inputs.make_qkv(B, L, n_q, n_kv, d, seed)
+    if mult != 1.0:
+        q = _bits_from_f32(inputs.bf16_to_f32(q) * np.float32(mult))
+    return q, k, v
+
+
+# ----------------------------------------------------------------------------
+# 50-digit brute force on tiny inputs ("Why Attention Scaling Breaks",
+# section "The O(n^2) problem": softmax(Q K^T / sqrt d) V; causal: each token
+# sees itself and earlier tokens; GQA: head h reads kv-head h // g)
+# ----------------------------------------------------------------------------
+def _brute_force(q, k, v, scale, causal):
+    mpmath = pytest.importorskip("mpmath")
+    mp = mpmath.mp
+    mp.dps = 50
+    B, n_q, L, d = q.shape
+    n_kv = k.shape[1]
+    g = n_q // n_kv
+    qv, kv_, vv = _vals(q), _vals(k), _vals(v)
+    sc = mp.mpf(float(np.float32(scale)))
+    out = np.zeros((B, n_q, L, d))
+    lse = np.zeros((B, n_q, L))
+    for b in range(B):
+        for h in range(n_q):
+            kh = h // g
+            for i in range(L):
+                keys = range(i + 1) if causal else range(L)
+                s = []
+                for j in keys:
+                    acc = mp.mpf(0)
+                    for t in range(d):
+                        acc += mp.mpf(qv[b, h, i, t]) * mp.mpf(kv_[b, kh, j, t])
+                    s.append(sc * acc)
+                # direct log-sum-exp: no max subtraction needed at 50 digits
+                z = mp.fsum([mp.e ** x for x in s])
+                lz = mp.log(z)
+                lse[b, h, i] = float(lz)
+                for t in range(d):
+                    o = mp.fsum([mp.e ** (x - lz) * mp.mpf(vv[b, kh, j, t])
+                                 for x, j in zip(s, keys)])
+                    out[b, h, i, t] = float(o)
+    return out, lse
+
+
+TINY = [
+    # B, L, n_q, n_kv, d, causal, scale
+    (1, 1, 1, 1, 1, 1, 0.5),
+    (1, 5, 2, 1, 3, 1, 0.37),
+    (2, 9, 4, 2, 8, 1, 1.0 / math.sqrt(8)),
+    (1, 9, 3, 1, 8, 0, 0.9),
+    (2, 7, 6, 2, 5, 0, 0.25),
+    (1, 8, 6, 3, 4, 1, 1.7),
+]
+
+
+@pytest.mark.parametrize("B,L,n_q,n_kv,d,causal,scale", TINY)
+def test_brute_force_50_digits(B, L, n_q, n_kv, d, causal, scale):
+    q, k, v = _random_case(B, L, n_q, n_kv, d, seed=11 + L * d + n_q)
+    ref_o, ref_l = _brute_force(q, k, v, scale, causal)
+    o, l, _ = oracle.attention_rows(q, k, v, scale, causal)
+    assert np.max(np.abs(o - ref_o.reshape(-1, d))) <= 1e-14
+    assert np.max(np.abs(l - ref_l.reshape(-1))) <= 1e-14
+
+
+def test_brute_force_large_scores():
+    # scores of several hundred: exp would overflow fp64 without the max
+    # subtraction ("Long-Context Attention Explained", safe-softmax remark)
+    B, L, n_q, n_kv, d = 1, 6, 2, 1, 4
+    q, k, v = _random_case(B, L, n_q, n_kv, d, seed=5)
+    q = _bits_from_f32(inputs.bf16_to_f32(q) * np.float32(300.0))
+    k = _bits_from_f32(inputs.bf16_to_f32(k) * np.float32(3.0))
+    ref_o, ref_l = _brute_force(q, k, v, 1.0, 1)
+    o, l, _ = oracle.attention_rows(q, k, v, 1.0, True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    assert np.max(np.abs(l)) > 710  # exp(lse) itself overflows fp64
+    assert np.max(np.abs(o - ref_o.reshape(-1, d))) <= 1e-14
+    assert np.max(np.abs(l - ref_l.reshape(-1)) / np.abs(ref_l.reshape(-1))) <= 1e-15
+
+
+# ----------------------------------------------------------------------------
+# closed forms and invariants
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [1, 0])
+def test_rows_sum_to_one_identity_v(causal):
+    # V = identity makes O equal the materialised weights P: rows sum to 1,
+    # masked weights are exactly 0 and visible ones are positive
+    L = d = 16
+    q, k, _ = _random_case(1, L, 2, 1, d, seed=3)
+    v = _bits_from_f32(np.eye(L, dtype=np.float32)[None, None])
+    o, _, _ = oracle.attention_rows(q, k, v, 0.3, causal)
+    o = o.reshape(2, L, L)
+    assert np.max(np.abs(o.sum(axis=-1) - 1.0)) <= 1e-13
+    for i in range(L):
+        vis = i + 1 if causal else L
+        assert np.all(o[:, i, :vis] > 0)
+        assert np.all(o[:, i, vis:] == 0.0)
+
+
+def test_constant_v_returns_v():
+    B, L, n_q, n_kv, d = 2, 33, 6, 3, 8
+    q, k, _ = _random_case(B, L, n_q, n_kv, d, seed=9)
+    c = np.zeros((B, n_kv, 1, d), dtype=np.float32)
+    for b in range(B):
+        for kv in range(n_kv):
+            c[b, kv, 0] = (kv + 1.5) * (-1.0) ** np.arange(d) + 0.25 * b
+    v = _bits_from_f32(np.broadcast_to(c, (B, n_kv, L, d)))
+    for causal in (1, 0):
+        o, _, _ = oracle.attention_rows(q, k, v, 0.2, causal)
+        o = o.reshape(B, n_q, L, d)
+        for h in range(n_q):
+            want = _vals(v)[:, h // (n_q // n_kv), 0, :]
+            assert np.max(np.abs(o[:, h] - want[:, None, :])) <= 1e-14
+
+
+def test_length_one_returns_v0():
+    B, n_q, n_kv, d = 2, 4, 2, 16
+    q, k, v = _random_case(B, 1, n_q, n_kv, d, seed=21)
+    scale = 0.125
+    for causal in (1, 0):
+        o, l, _ = oracle.attention_rows(q, k, v, scale, causal)
+        o = o.reshape(B, n_q, d)
+        l = l.reshape(B, n_q)
+        for b in range(B):
+            for h in range(n_q):
+                kv = h // 2
+                assert np.array_equal(o[b, h], _vals(v)[b, kv, 0])
+                want = float(np.float32(scale)) * float(
+                    np.dot(_vals(q)[b, h, 0], _vals(k)[b, kv, 0]))
+                assert abs(l[b, h] - want) <= 1e-14 * max(1.0, abs(want))
+
+
+def test_first_causal_row_returns_v0():
+    B, L, n_q, n_kv, d = 1, 40, 4, 4, 32
+    q, k, v = _random_case(B, L, n_q, n_kv, d, seed=22)
+    o, l, _ = oracle.attention_rows(q, k, v, 0.177, True)
+    o = o.reshape(B, n_q, L, d)
+    l = l.reshape(B, n_q, L)
+    for h in range(n_q):
+        assert np.array_equal(o[0, h, 0], _vals(v)[0, h, 0])
+        want = float(np.float32(0.177)) * float(np.dot(_vals(q)[0, h, 0], _vals(k)[0, h, 0]))
+        assert abs(l[0, h, 0] - want) <= 1e-14 * max(1.0, abs(want))
+
+
+def test_zero_query_gives_running_mean():
+    # all scores equal: causal row i is the mean of V[0..i], LSE = ln(i + 1)
+    B, L, n_q, n_kv, d = 1, 50, 2, 1, 8
+    _, k, v = _random_case(B, L, n_q, n_kv, d, seed=23)
+    q = np.zeros((B, n_q, L, d), dtype=np.uint16)
+    vv = _vals(v)[0, 0]
+    o, l, _ = oracle.attention_rows(q, k, v, 0.5, True)
+    o = o.reshape(n_q, L, d)
+    l = l.reshape(n_q, L)
+    means = np.cumsum(vv, axis=0) / np.arange(1, L + 1)[:, None]
+    for h in range(n_q):
+        assert np.max(np.abs(o[h] - means)) <= 1e-14
+        assert np.max(np.abs(l[h] - np.log(np.arange(1, L + 1)))) <= 1e-14
+    o, l, _ = oracle.attention_rows(q, k, v, 0.5, False)
+    assert np.max(np.abs(o - vv.mean(axis=0))) <= 1e-14
+    assert np.max(np.abs(l - math.log(L))) <= 1e-14
+
+
+def test_causal_rows_are_noncausal_prefixes():
+    B, L, n_q, n_kv, d = 1, 24, 2, 1, 8
+    q, k, v = _random_case(B, L, n_q, n_kv, d, seed=24)
+    oc, lc, _ = oracle.attention_rows(q, k, v, 0.3, True)
+    oc = oc.reshape(n_q, L, d)
+    lc = lc.reshape(n_q, L)
+    onc, lnc, _ = oracle.attention_rows(q, k, v, 0.3, False)
+    onc = onc.reshape(n_q, L, d)
+    lnc = lnc.reshape(n_q, L)
+    assert np.max(np.abs(oc[:, L - 1] - onc[:, L - 1])) <= 1e-15
+    assert np.max(np.abs(lc[:, L - 1] - lnc[:, L - 1])) <= 1e-15
+    assert np.max(np.abs(oc[:, :L - 1] - onc[:, :L - 1])) > 1e-3  # the mask matters
+    for i in (0, 1, 7, 15, 22):
+        op, lp, _ = oracle.attention_rows(
+            np.ascontiguousarray(q[:, :, :i + 1]), np.ascontiguousarray(k[:, :, :i + 1]),
+            np.ascontiguousarray(v[:, :, :i + 1]), 0.3, False)
+        op = op.reshape(n_q, i + 1, d)
+        lp = lp.reshape(n_q, i + 1)
+        assert np.max(np.abs(op[:, i] - oc[:, i])) <= 1e-15
+        assert np.max(np.abs(lp[:, i] - lc[:, i])) <= 1e-15
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    B, L, n_q, n_kv, d = 2, 31, 8, 2, 16
+    g = n_q // n_kv
+    q, k, v = _random_case(B, L, n_q, n_kv, d, seed=25)
+    og, lg, _ = oracle.attention_rows(q, k, v, 0.25, True)
+    kr = np.ascontiguousarray(np.repeat(k, g, axis=1))
+    vr = np.ascontiguousarray(np.repeat(v, g, axis=1))
+    om, lm, _ = oracle.attention_rows(q, kr, vr, 0.25, True)
+    assert np.array_equal(og, om) and np.array_equal(lg, lm)
+    # the other grouping (head h -> kv-head h mod n_kv) is a different model
+    kt = np.ascontiguousarray(np.tile(k, (1, g, 1, 1)))
+    vt = np.ascontiguousarray(np.tile(v, (1, g, 1, 1)))
+    ot, _, _ = oracle.attention_rows(q, kt, vt, 0.25, True)
+    assert np.max(np.abs(ot - og)) > 1e-3
+
+
+def test_batch_independence():
+    B, L, n_q, n_kv, d = 2, 17, 4, 2, 8
+    q, k, v = _random_case(B, L, n_q, n_kv, d, seed=26)
+    o, l, _ = oracle.attention_rows(q, k, v, 0.4, True)
+    o = o.reshape(B, -1)
+    l = l.reshape(B, -1)
+    for b in range(B):
+        ob, lb, _ = oracle.attention_rows(q[b:b + 1], k[b:b + 1], v[b:b + 1], 0.4, True)
+        assert np.array_equal(ob.reshape(-1), o[b]) and np.array_equal(lb, l[b])
+
+
+def test_selected_rows_match_full_run():
+    B, L, n_q, n_kv, d = 1, 64, 6, 2, 16
+    q, k, v = _random_case(B, L, n_q, n_kv, d, seed=27)
+    o, l, f = oracle.attention_rows(q, k, v, 0.25, True)
+    rows = inputs.sample_rows(B, n_q, L, 50, seed=3, block_rows=32)
+    os_, ls, fs = oracle.attention_rows(q, k, v, 0.25, True, rows=rows)
+    assert np.array_equal(os_, o[rows]) and np.array_equal(ls, l[rows])
+    i = rows % L
+    assert fs == int(np.sum(4 * d * (i + 1)))
+
+
+# ----------------------------------------------------------------------------
+# library special case: torch SDPA on the CPU in fp64 ("Long-Context
+# Attention Explained": SDPA on a CPU matched the plain version to 4.4e-16,
+# 8.9e-16 with is_causal=True)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [1, 0])
+def test_torch_sdpa_fp64(causal):
+    torch = pytest.importorskip("torch")
+    B, L, n_q, n_kv, d = 2, 129, 8, 2, 64
+    q, k, v = _random_case(B, L, n_q, n_kv, d, seed=31)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, l, _ = oracle.attention_rows(q, k, v, scale, causal)
+    tq, tk, tv = (torch.from_numpy(_vals(x)) for x in (q, k, v))
+    g = n_q // n_kv
+    tk_r = tk.repeat_interleave(g, dim=1)
+    tv_r = tv.repeat_interleave(g, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk_r, tv_r, is_causal=bool(causal), scale=scale)
+    assert np.max(np.abs(o - ref.reshape(-1, d).numpy())) <= 1e-12
+    s = torch.matmul(tq, tk_r.transpose(-1, -2).contiguous()) * scale
+    if causal:
+        mask = torch.ones(L, L, dtype=torch.bool).tril()
+        s = s.masked_fill(~mask, float("-inf"))
+    ref_lse = torch.logsumexp(s, dim=-1).reshape(-1).numpy()
+    assert np.max(np.abs(l - ref_lse)) <= 1e-12
+
+
+# ----------------------------------------------------------------------------
+# exactness of the tiled algorithm: an independent fp64 online softmax with
+# queries in the outer loop ("Long-Context Attention Explained", sections
+# "Tiling" and "Online softmax", five steps), block sizes from the check ledger
+# ----------------------------------------------------------------------------
+def _tiled_online_softmax(qv, kv, vv, scale, causal, block):
+    """One head, fp64: keep m, l, acc per row; rescale by e^(m_old - m_new)."""
+    L, d = qv.shape
+    out = np.zeros((L, d))
+    lse = np.zeros(L)
+    for i0 in range(0, L, block):
+        qi = qv[i0:i0 + block]
+        rows = np.arange(i0, i0 + len(qi))
+        m = np.full(len(qi), -np.inf)
+        l = np.zeros(len(qi))
+        acc = np.zeros((len(qi), d))
+        for j0 in range(0, L, block):
+            if causal and j0 > rows[-1]:
+                break  # every key of this tile is after every query
+            s = (qi @ kv[j0:j0 + block].T) * scale
+            if causal:
+                cols = np.arange(j0, j0 + s.shape[1])
+                s = np.where(cols[None, :] <= rows[:, None], s, -np.inf)
+            m_new = np.maximum(m, s.max(axis=1))
+            fix = np.exp(m - m_new)
+            p = np.exp(s - m_new[:, None])
+            l = l * fix + p.sum(axis=1)
+            acc = acc * fix[:, None] + p @ vv[j0:j0 + block]
+            m = m_new
+        out[i0:i0 + len(qi)] = acc / l[:, None]
+        lse[i0:i0 + len(qi)] = m + np.log(l)
+    return out, lse
+
+
+def test_tiled_online_softmax_matches_oracle_ledger_bound():
+    ledger = json.load(open(GOLDEN))["check_ledger"]["block_sizes_fp64"]
+    L, d = ledger["N"], 64
+    q, k, v = _random_case(1, L, 1, 1, d, seed=41)
+    o, l, _ = oracle.attention_rows(q, k, v, 1 / math.sqrt(d), False)
+    sc = float(np.float32(1 / math.sqrt(d)))
+    for block in ledger["blocks"]:
+        to, tl = _tiled_online_softmax(_vals(q)[0, 0], _vals(k)[0, 0], _vals(v)[0, 0],
+                                       sc, False, block)
+        assert np.max(np.abs(to - o)) <= ledger["bound"], block
+        assert np.max(np.abs(tl - l)) <= 1e-13
+
+
+@pytest.mark.parametrize("block", [1, 7, 32, 64, 128, 200])
+def test_tiled_online_softmax_causal(block):
+    L, d = 200, 64
+    q, k, v = _random_case(1, L, 1, 1, d, seed=42)
+    sc = float(np.float32(0.125))
+    o, l, _ = oracle.attention_rows(q, k, v, sc, True)
+    to, tl = _tiled_online_softmax(_vals(q)[0, 0], _vals(k)[0, 0], _vals(v)[0, 0],
+                                   sc, True, block)
+    assert np.max(np.abs(to - o)) <= 1e-13
+    assert np.max(np.abs(tl - l)) <= 1e-13
+
+
+def test_ledger_example_magnitude():
+    # the teaching run: N = 1024, d = 64, block 64, tiled vs plain differ by
+    # rounding only (the page printed 3.9e-16 on its own inputs)
+    ledger = json.load(open(GOLDEN))["check_ledger"]["tiled_vs_naive_fp64"]
+    L, d = ledger["N"], ledger["d"]
+    q, k, v = _random_case(1, L, 1, 1, d, seed=0)
+    sc = float(np.float32(1 / math.sqrt(d)))
+    o, _, _ = oracle.attention_rows(q, k, v, sc, False)
+    to, _ = _tiled_online_softmax(_vals(q)[0, 0], _vals(k)[0, 0], _vals(v)[0, 0],
+                                  sc, False, ledger["block"])
+    assert np.max(np.abs(to - o)) <= 10 * ledger["max_abs"]
+
+
+# ----------------------------------------------------------------------------
+# flop count ("flops / prefill-attention": 2 * n_q * d_h * L^2 causal; the
+# exact visible-pair count is L(L+1)/2 per head)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("B,L,n_q,n_kv,d", [(1, 37, 4, 2, 8), (2, 64, 6, 3, 16)])
+def test_flop_count(B, L, n_q, n_kv, d):
+    q, k, v = _random_case(B, L, n_q, n_kv, d, seed=51)
+    _, _, fc = oracle.attention_rows(q, k, v, 0.3, True)
+    assert fc == 2 * B * n_q * d * L * (L + 1)
+    page_f = 2 * n_q * d * L * L * B
+    assert fc == page_f + page_f // L  # F * (1 + 1/L)
+    _, _, fn = oracle.attention_rows(q, k, v, 0.3, False)
+    assert fn == 4 * B * n_q * d * L * L
+
+
+def test_large_scores_stay_finite():
+    # Q x 20 pushes scores past 150 ("Long-Context Attention Explained",
+    # check ledger: scores of 162 made an unsafe softmax produce NaN)
+    B, L, n_q, n_kv, d = 1, 256, 2, 1, 64
+    q, k, v = _random_case(B, L, n_q, n_kv, d, seed=61, mult=20.0)
+    o, l, _ = oracle.attention_rows(q, k, v, 0.25, True)
+    qv, kv = _vals(q)[0, 0], _vals(k)[0, 0]
+    assert np.max(np.abs(qv @ kv.T * 0.25)) > 150
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    assert np.max(np.abs(o)) <= np.max(np.abs(_vals(v))) + 1e-12
+
+
+def test_bad_arguments_rejected():
+    q, k, v = _random_case(1, 4, 3, 2, 4, seed=1)  # 3 % 2 != 0
+    with pytest.raises(ValueError):
+        oracle.attention_rows(q, k, v, 0.5, True)
+    q, k, v = _random_case(1, 4, 2, 1, 4, seed=1)
+    with pytest.raises(ValueError):
+        oracle.attention_rows(q, k, v, float("nan"), True)
+    with pytest.raises(ValueError):
+        oracle.attention_rows(q, k, v, 0.5, True, rows=np.array([8], dtype=np.int64))
