@@ -1,0 +1,121 @@
+"""ctypes binding for libattn_prefill.so (argument marshalling only).
+
+Every step of the attention runs in the HIP kernels of the library; this
+module checks tensor properties, allocates outputs with torch (the caller owns
+them) and passes raw device pointers plus the current HIP stream across the
+C ABI declared in include/attn_prefill.h.  There is no CPU fallback: if the
+library is missing or fails to load, the first call raises.
+"""
+import ctypes
+import math
+import os
+
+from . import _build
+
+ATTN_PREFILL_OK = 0
+
+_lib = None
+
+
+class AttnPrefillError(RuntimeError):
+    """A nonzero status from attn_prefill_fwd (text from attn_prefill_strerror)."""
+
+    def __init__(self, status, text):
+        super().__init__(f"attn_prefill_fwd failed ({status}): {text}")
+        self.status = status
+
+
+def library():
+    """Load libattn_prefill.so once and declare the exported signatures."""
+    global _lib
+    if _lib is None:
+        path = os.environ.get("ATTN_PREFILL_LIB", _build.LIB)
+        if not os.path.exists(path):
+            raise ImportError(
+                f"{path} is missing: build it first (python -c "
+                "'import __graft_entry__ as g; g.build()' or python "
+                "causal_gqa_prefill_amd/_build.py); there is no fallback")
+        lib = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        ci = ctypes.c_int
+        lib.attn_prefill_fwd.restype = ci
+        lib.attn_prefill_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci,
+                                         ctypes.c_float, ci, vp]
+        lib.attn_prefill_strerror.restype = ctypes.c_char_p
+        lib.attn_prefill_strerror.argtypes = [ci]
+        lib.attn_prefill_version.restype = ci
+        lib.attn_prefill_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return library().attn_prefill_strerror(int(status)).decode()
+
+
+def fwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, L, n_q, n_kv, d_h,
+            scale, causal, stream_ptr):
+    """Direct call of attn_prefill_fwd with integer pointers; returns status."""
+    return library().attn_prefill_fwd(
+        ctypes.c_void_p(q_ptr), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
+        ctypes.c_void_p(out_ptr), ctypes.c_void_p(lse_ptr),
+        int(B), int(L), int(n_q), int(n_kv), int(d_h), float(scale), int(causal),
+        ctypes.c_void_p(stream_ptr))
+
+
+def _check(q, k, v):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, heads, L, d_h]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on the same device")
+    B, n_q, L, d_h = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != L or k.shape[3] != d_h:
+        raise ValueError(f"k and v must be [B, n_kv, L, d_h] matching q {tuple(q.shape)}; "
+                         f"got k {tuple(k.shape)}, v {tuple(v.shape)}")
+    return B, n_q, k.shape[1], L, d_h
+
+
+def attn_prefill_into(q, k, v, out, lse, scale=None, causal=True, stream=None):
+    """Run the forward pass into caller-provided out (bf16) and lse (fp32)."""
+    import torch
+    B, n_q, n_kv, L, d_h = _check(q, k, v)
+    if out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, n_q, L) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, n_q, L]")
+    if out.device != q.device or lse.device != q.device:
+        raise ValueError("out and lse must be on the inputs' device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_h)
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        status = fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                         lse.data_ptr(), B, L, n_q, n_kv, d_h, scale, int(bool(causal)),
+                         s.cuda_stream)
+    if status != ATTN_PREFILL_OK:
+        raise AttnPrefillError(status, strerror(status))
+    return out, lse
+
+
+def attn_prefill(q, k, v, scale=None, causal=True, stream=None):
+    """Causal (or full) GQA prefill attention forward.
+
+    q: bf16 [B, n_q, L, d_h]; k, v: bf16 [B, n_kv, L, d_h] (contiguous, HIP
+    device).  scale defaults to 1/sqrt(d_h).  Returns (out bf16 like q,
+    lse fp32 [B, n_q, L]), enqueued on `stream` (default: current stream).
+    """
+    import torch
+    B, n_q, _, L, _ = _check(q, k, v)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, n_q, L), dtype=torch.float32, device=q.device)
+    return attn_prefill_into(q, k, v, out, lse, scale=scale, causal=causal, stream=stream)

@@ -16,8 +16,12 @@ def bf16_bits(x) -> np.ndarray:
 
     Finite inputs only (the generators never produce NaN or Inf)."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
-    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    t = np.right_shift(u, np.uint32(16))      # one temporary, updated in place
+    np.bitwise_and(t, np.uint32(1), out=t)
+    np.add(t, np.uint32(0x7FFF), out=t)
+    np.add(t, u, out=t)
+    np.right_shift(t, np.uint32(16), out=t)
+    return t.astype(np.uint16)
 
 
 def bf16_to_f32(bits) -> np.ndarray:

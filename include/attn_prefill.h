@@ -1,0 +1,101 @@
+/*
+ * attn_prefill.h -- C ABI of the MI355X (gfx950) causal GQA prefill attention
+ * forward pass (libattn_prefill.so).
+ *
+ * The operation.  For every batch b, query head h and query position i:
+ *     s_j    = scale * sum_t Q[b,h,i,t] * K[b,kv,j,t]      for visible j
+ *     O[b,h,i,:] = sum_j softmax(s)_j * V[b,kv,j,:]
+ *     LSE[b,h,i] = ln sum_j exp(s_j)
+ * with kv = floor(h / g), g = n_q / n_kv.
+ *   - Scaled dot-product attention softmax(Q K^T / sqrt(d)) V: "Why Attention
+ *     Scaling Breaks", section "The O(n^2) problem", and "Long-Context
+ *     Attention Explained", section on quadratic cost.
+ *   - Causal visibility: a token looks only backwards, itself included, so
+ *     key j is visible to query i iff j <= i ("Long-Context Attention
+ *     Explained", quadratic-cost section).  causal = 0 makes all L keys
+ *     visible.
+ *   - Grouped-query heads: n_q query heads share n_kv key/value heads ("flops /
+ *     prefill-attention", section "Arithmetic intensity"); query head h reads
+ *     key/value head floor(h / g), consecutive query heads forming a group.
+ *   - The score matrix never reaches memory: tiles of keys are streamed past
+ *     each block of queries with an online softmax ("Why Attention Scaling
+ *     Breaks", section "Flash Attention: the tiling insight"; "Long-Context
+ *     Attention Explained", sections "Tiling" and "Online softmax"); the
+ *     result equals the plain definition up to rounding.
+ *   - LSE is the per-row statistic a backward pass recomputes from
+ *     ("Long-Context Attention Explained", section "What FlashAttention does
+ *     not change"): natural log, of the scaled scores, fp32.
+ *
+ * Layouts (all row-major, contiguous, d_h fastest):
+ *   q, out : bf16 [B, n_q,  L, d_h]
+ *   k, v   : bf16 [B, n_kv, L, d_h]
+ *   lse    : fp32 [B, n_q,  L]
+ * bf16 is the 16-bit brain-float format (the upper half of an IEEE fp32).
+ *
+ * Numerics: Q K^T and P V run as bf16 matrix-core products with fp32
+ * accumulation; the softmax runs in fp32; P is rounded to bf16 (nearest even)
+ * before P V; O is rounded to bf16 (nearest even) once, after the division by
+ * the row sum.
+ *
+ * Ownership: the caller allocates and frees all five buffers, on the device
+ * that is current when the call is made and that `stream` belongs to.  The
+ * library allocates nothing, keeps no state between calls, never
+ * synchronises, and may be called from several host threads at once.  out and
+ * lse must not overlap each other or any input.
+ *
+ * Errors: every argument is checked on the host before anything is enqueued.
+ * A nonzero return means nothing was enqueued, except ATTN_PREFILL_ERR_LAUNCH,
+ * which reports the HIP launch error.  Faults inside the kernel surface at the
+ * caller's next synchronisation, as for any HIP kernel.
+ */
+#ifndef ATTN_PREFILL_H
+#define ATTN_PREFILL_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_prefill_status {
+    ATTN_PREFILL_OK = 0,
+    ATTN_PREFILL_ERR_NULL_PTR = 1,      /* a buffer pointer is NULL            */
+    ATTN_PREFILL_ERR_BAD_SHAPE = 2,     /* B, L, n_q or n_kv < 1               */
+    ATTN_PREFILL_ERR_BAD_GQA = 3,       /* n_q is not a multiple of n_kv       */
+    ATTN_PREFILL_ERR_BAD_HEADDIM = 4,   /* d_h is not 64 or 128                */
+    ATTN_PREFILL_ERR_BAD_SCALE = 5,     /* scale is NaN or infinite            */
+    ATTN_PREFILL_ERR_BAD_CAUSAL = 6,    /* causal is not 0 or 1                */
+    ATTN_PREFILL_ERR_MISALIGNED = 7,    /* q/k/v/out not 16-byte aligned, or
+                                           lse not 4-byte aligned              */
+    ATTN_PREFILL_ERR_SIZE_OVERFLOW = 8, /* a size or the grid overflows        */
+    ATTN_PREFILL_ERR_ALIASING = 9,      /* out or lse overlaps another buffer  */
+    ATTN_PREFILL_ERR_LAUNCH = 10        /* the HIP launch failed               */
+};
+
+/*
+ * Causal (or full) GQA prefill attention forward pass.
+ *   q, k, v : device pointers to the bf16 inputs (layouts above)
+ *   out     : device pointer, bf16 [B, n_q, L, d_h], written entirely
+ *   lse     : device pointer, fp32 [B, n_q, L], written entirely
+ *   B, L, n_q, n_kv, d_h : sizes; n_q % n_kv == 0; d_h in {64, 128}
+ *   scale   : multiplies Q K^T (1/sqrt(d_h) for standard attention); any
+ *             finite value
+ *   causal  : 1 = key j visible to query i iff j <= i; 0 = all keys visible
+ *   stream  : HIP stream the work is enqueued on (0 = the null stream)
+ * Returns ATTN_PREFILL_OK once the work is enqueued, else an error code.
+ */
+int attn_prefill_fwd(const void *q, const void *k, const void *v, void *out,
+                     float *lse, int B, int L, int n_q, int n_kv, int d_h,
+                     float scale, int causal, hipStream_t stream);
+
+/* Static text for a status code (never NULL). */
+const char *attn_prefill_strerror(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int attn_prefill_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_PREFILL_H */

@@ -1,0 +1,59 @@
+"""The C-ABI library loads without a GPU, exports every symbol its header
+declares, and rejects bad arguments on the host before any HIP call."""
+import os
+import re
+
+import pytest
+
+from causal_gqa_prefill_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_prefill.h")
+
+ALIGNED = 0x100000  # never dereferenced: validation fails first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_prefill_\w+)\s*\(", text)))
+
+
+def test_library_exports_header_symbols():
+    lib = binding.library()
+    names = _declared_functions()
+    assert names == ["attn_prefill_fwd", "attn_prefill_strerror", "attn_prefill_version"]
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror():
+    assert binding.library().attn_prefill_version() >= 100
+    for code in range(0, 11):
+        assert binding.strerror(code) not in ("", "unknown status")
+    assert binding.strerror(99) == "unknown status"
+
+
+def _call(**kw):
+    args = dict(q=ALIGNED, k=ALIGNED + 0x10000000, v=ALIGNED + 0x20000000,
+                out=ALIGNED + 0x30000000, lse=ALIGNED + 0x40000000,
+                B=1, L=128, n_q=4, n_kv=4, d_h=64, scale=0.125, causal=1, stream=0)
+    args.update(kw)
+    return binding.fwd_raw(args["q"], args["k"], args["v"], args["out"], args["lse"],
+                           args["B"], args["L"], args["n_q"], args["n_kv"], args["d_h"],
+                           args["scale"], args["causal"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(out=0), 1), (dict(lse=0), 1),
+    (dict(B=0), 2), (dict(L=0), 2), (dict(n_q=-1), 2), (dict(n_kv=0), 2),
+    (dict(n_q=6, n_kv=4), 3),
+    (dict(d_h=96), 4), (dict(d_h=256), 4), (dict(d_h=0), 4),
+    (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5),
+    (dict(causal=2), 6), (dict(causal=-1), 6),
+    (dict(q=ALIGNED + 8), 7), (dict(out=ALIGNED + 0x30000002), 7), (dict(lse=ALIGNED + 0x40000002), 7),
+    (dict(B=1 << 30, n_q=1 << 30, n_kv=1 << 30, L=1 << 30), 8),
+    (dict(out=ALIGNED), 9), (dict(lse=ALIGNED + 0x10000010), 9), (dict(lse=ALIGNED + 0x30000100), 9),
+])
+def test_bad_arguments_rejected_on_host(kw, code):
+    assert _call(**kw) == code

@@ -1,0 +1,190 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from causal_gqa_prefill_amd import inputs
+from causal_gqa_prefill_amd.configs import CONFIGS
+
+from gpu_util import compare, from_dev_bf16, run_gpu, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from causal_gqa_prefill_amd import binding
+    binding.library()  # raises if the HIP library is missing: no fallback
+
+
+def _check_case(B, L, n_q, n_kv, d, causal, scale, seed, rows=None, name=None):
+    name = name or f"B={B} L={L} n_q={n_q} n_kv={n_kv} d={d} causal={causal} scale={scale:.4g}"
+    say(f"case {name}")
+    qb, kb, vb = inputs.make_qkv(B, L, n_q, n_kv, d, seed)
+    o, l = run_gpu(qb, kb, vb, scale, causal)
+    ref_o, ref_l, _ = oracle.attention_rows(qb, kb, vb, scale, causal, rows=rows)
+    o = o.reshape(-1, d)
+    l = l.reshape(-1)
+    if rows is not None:
+        o, l = o[rows], l[rows]
+    compare(name, o, l, ref_o, ref_l)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads: every row for configs 1-3, 4096 seeded rows for 4-5
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", CONFIGS, ids=[f"config{c.index}" for c in CONFIGS])
+def test_config_parity(cfg):
+    say(f"config {cfg.index}: {cfg.describe()}")
+    qb, kb, vb = inputs.make_config_qkv(cfg)
+    o, l = run_gpu(qb, kb, vb, cfg.scale, cfg.causal)
+    o = o.reshape(-1, cfg.d_h)
+    l = l.reshape(-1)
+    if cfg.sampled_rows:
+        rows = inputs.sample_rows(cfg.B, cfg.n_q, cfg.L, cfg.sampled_rows, cfg.seed)
+        ref_o, ref_l, _ = oracle.attention_rows(qb, kb, vb, cfg.scale, cfg.causal, rows=rows)
+        compare(f"config{cfg.index} sampled", o[rows], l[rows], ref_o, ref_l)
+    else:
+        # every row, one head-chunk at a time so progress shows
+        total = cfg.B * cfg.n_q * cfg.L
+        chunk = max(cfg.L, total // 8)
+        for r0 in range(0, total, chunk):
+            rows = np.arange(r0, min(total, r0 + chunk), dtype=np.int64)
+            ref_o, ref_l, _ = oracle.attention_rows(qb, kb, vb, cfg.scale, cfg.causal, rows=rows)
+            compare(f"config{cfg.index} rows {r0}..{rows[-1]}", o[rows], l[rows], ref_o, ref_l)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+# ---------------------------------------------------------------------------
+# edge shapes: ragged L, every GQA ratio class, both head sizes, B > 1,
+# non-causal, scales other than 1/sqrt(d)
+# ---------------------------------------------------------------------------
+EDGE = [
+    # B, L, n_q, n_kv, d, causal, scale
+    (1, 1, 4, 4, 64, 1, None),
+    (1, 2, 8, 2, 128, 1, None),
+    (1, 15, 6, 1, 128, 1, None),
+    (1, 63, 4, 1, 64, 1, None),
+    (1, 64, 8, 8, 128, 1, None),
+    (1, 65, 16, 2, 128, 1, None),
+    (3, 127, 4, 2, 64, 1, None),
+    (1, 129, 12, 2, 128, 1, None),
+    (2, 257, 3, 1, 128, 1, None),
+    (1, 1000, 8, 1, 128, 1, None),
+    (1, 4097, 6, 6, 64, 1, None),
+    (1, 1, 2, 1, 128, 0, None),
+    (1, 65, 8, 2, 64, 0, None),
+    (2, 300, 4, 4, 128, 0, None),
+    (1, 777, 16, 4, 128, 0, 0.3),
+    (1, 200, 4, 2, 128, 1, 0.5),
+    (1, 200, 4, 2, 64, 1, 0.0),
+    (1, 200, 4, 2, 128, 1, -0.0883883),
+    (1, 130, 5, 5, 128, 1, None),
+    (1, 96, 24, 3, 64, 1, None),
+]
+
+
+@pytest.mark.parametrize("B,L,n_q,n_kv,d,causal,scale", EDGE)
+def test_edge_shapes(B, L, n_q, n_kv, d, causal, scale):
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+    _check_case(B, L, n_q, n_kv, d, causal, scale, seed=2000 + L + 7 * n_q + d)
+
+
+# ---------------------------------------------------------------------------
+# closed forms on the GPU
+# ---------------------------------------------------------------------------
+def test_constant_v_gpu():
+    B, L, n_q, n_kv, d = 1, 300, 8, 2, 128
+    qb, kb, _ = inputs.make_qkv(B, L, n_q, n_kv, d, seed=31)
+    c = np.zeros((B, n_kv, L, d), dtype=np.float32)
+    c[:, 0] = 1.5
+    c[:, 1] = -0.75
+    vb = inputs.bf16_bits(c)
+    o, l = run_gpu(qb, kb, vb, 0.088, True)
+    want = np.where(np.arange(n_q) // 4 == 0, 1.5, -0.75)[None, :, None, None]
+    assert np.max(np.abs(o - want)) <= 1e-2
+
+
+def test_zero_query_gpu():
+    B, L, n_q, n_kv, d = 1, 500, 4, 1, 64
+    _, kb, vb = inputs.make_qkv(B, L, n_q, n_kv, d, seed=32)
+    qb = np.zeros((B, n_q, L, d), dtype=np.uint16)
+    o, l = run_gpu(qb, kb, vb, 0.125, True)
+    vv = inputs.bf16_to_f32(vb)[0, 0].astype(np.float64)
+    means = np.cumsum(vv, axis=0) / np.arange(1, L + 1)[:, None]
+    assert np.max(np.abs(o[0] - means[None])) <= 1e-2
+    assert np.max(np.abs(l[0] - np.log(np.arange(1, L + 1))[None])) <= 1e-3
+
+
+def test_first_row_is_v0_gpu():
+    B, L, n_q, n_kv, d = 2, 130, 4, 2, 128
+    qb, kb, vb = inputs.make_qkv(B, L, n_q, n_kv, d, seed=33)
+    o, _ = run_gpu(qb, kb, vb, 0.088, True)
+    vv = inputs.bf16_to_f32(vb).astype(np.float64)
+    for h in range(n_q):
+        assert np.array_equal(o[:, h, 0], vv[:, h // 2, 0])  # P = 1 exactly
+
+
+def test_gqa_equals_repeated_kv_gpu():
+    B, L, n_q, n_kv, d = 1, 333, 8, 2, 128
+    qb, kb, vb = inputs.make_qkv(B, L, n_q, n_kv, d, seed=34)
+    og, lg = run_gpu(qb, kb, vb, 0.088, True)
+    kr = np.ascontiguousarray(np.repeat(kb, 4, axis=1))
+    vr = np.ascontiguousarray(np.repeat(vb, 4, axis=1))
+    om, lm = run_gpu(qb, kr, vr, 0.088, True)
+    assert np.max(np.abs(og - om)) <= 1e-2 and np.max(np.abs(lg - lm)) <= 1e-4
+
+
+def test_large_scores_gpu():
+    # Q x 20: scores beyond 150 must not overflow the softmax
+    B, L, n_q, n_kv, d = 1, 512, 4, 2, 128
+    qb, kb, vb = inputs.make_qkv(B, L, n_q, n_kv, d, seed=35)
+    qb = inputs.bf16_bits(inputs.bf16_to_f32(qb) * np.float32(20.0))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, l = run_gpu(qb, kb, vb, scale, True)
+    ref_o, ref_l, _ = oracle.attention_rows(qb, kb, vb, scale, True)
+    compare("large scores", o.reshape(-1, d), l.reshape(-1), ref_o, ref_l)
+
+
+# ---------------------------------------------------------------------------
+# robustness: determinism, streams, argument errors
+# ---------------------------------------------------------------------------
+def test_bitwise_deterministic():
+    import torch
+    from causal_gqa_prefill_amd import attn_prefill
+    qb, kb, vb = inputs.make_qkv(1, 1000, 8, 2, 128, seed=36)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    outs = [attn_prefill(q, k, v) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l, outs[0][1])
+
+
+def test_non_default_stream():
+    import torch
+    qb, kb, vb = inputs.make_qkv(1, 700, 4, 1, 128, seed=37)
+    s = torch.cuda.Stream()
+    o, l = run_gpu(qb, kb, vb, 0.088, True, stream=s)
+    ref_o, ref_l, _ = oracle.attention_rows(qb, kb, vb, 0.088, True)
+    compare("side stream", o.reshape(-1, 128), l.reshape(-1), ref_o, ref_l)
+
+
+def test_argument_errors_raise():
+    import torch
+    from causal_gqa_prefill_amd import AttnPrefillError, attn_prefill
+    q = torch.zeros((1, 6, 64, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 4, 64, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(AttnPrefillError):
+        attn_prefill(q, k, k.clone())  # 6 % 4 != 0
+    q = torch.zeros((1, 4, 64, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(AttnPrefillError):
+        attn_prefill(q, q.clone(), q.clone())  # d_h = 96
+    with pytest.raises(TypeError):
+        attn_prefill(q.float(), q.float(), q.float())
