@@ -13,6 +13,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # keep the compiler from emitting packed fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the softmax reads the scores straight from the
+    # MFMA destination instead of copying them out of AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall",
 ]
 

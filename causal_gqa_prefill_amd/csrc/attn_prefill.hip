@@ -16,32 +16,44 @@
 //    visited; only tiles that straddle the diagonal are masked ("flops /
 //    prefill-attention", section "Workarounds"; "Long-Context Attention
 //    Explained", causal block skipping).
-//  * Grouped-query heads: the g query heads of one key/value head read the
-//    same K/V tile from LDS, so K and V bytes are amortised over g heads
+//  * Grouped-query heads: the query heads of one key/value head read the
+//    same K/V tile from LDS, so K and V bytes are amortised over the group
 //    ("flops / prefill-attention", section "Arithmetic intensity").
 //
 // CDNA4 mapping:
-//  * A workgroup is 8 wave64s.  Each wave owns 32 query rows of one head.  A
-//    workgroup covers HW heads of one group times BR = 256 / HW rows, so the
-//    K/V tile it stages in LDS is used by HW heads.
+//  * A workgroup is 4 wave64s, one per SIMD, covering 256 query columns:
+//    HWG heads of one group times BR = 256 / HWG rows.  Each wave owns two
+//    blocks of 32 columns, so every K or V operand fragment it reads from LDS
+//    feeds two MFMAs (LDS delivers 128 B/clk/CU; one fragment per MFMA would
+//    use all of it at the MFMA peak).
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand, Q (held in
-//    VGPRs for the whole loop) the B operand.  In the 32x32 result, lane l
+//    VGPRs for the whole loop) the B operand.  In the 32x32 result lane l
 //    holds 16 keys of query column l % 32, so the row max and row sum are
-//    lane-local except for one exchange between lanes l and l ^ 32.
-//  * The output is accumulated transposed, O^T += V^T P^T, with V^T (from
-//    LDS) as the A operand and P^T as the B operand.  The score result's
-//    register layout is used directly as the B operand: the 16 keys a lane
-//    holds form the contraction slots of two k-steps in a permuted order,
-//    and V^T is written to LDS in that same key order, so P never leaves the
-//    registers.
-//  * LDS tiles are XOR-swizzled in 16-byte chunks so both the 16-byte MFMA
-//    operand reads and the tile writes are free of bank conflicts (the V^T
-//    transposing writes are 4-way conflicted but are few).
-//  * K/V tiles are double-buffered: the global loads of tile t+1 are in
-//    flight while tile t is computed; one barrier per tile.
-//  * exp is done as exp2 with scale*log2(e) folded into one FMA; LSE is
-//    converted back to the natural log at the end.
+//    lane-local except for one exchange between lanes l and l ^ 32
+//    (v_permlane32_swap).
+//  * The output is accumulated transposed, O^T += V^T P^T, with V^T as the A
+//    operand and P^T as the B operand.  The score result's register layout
+//    is used directly as the B operand (the 16 keys a lane holds are the
+//    contraction slots of two k-steps, in a permuted key order), so P never
+//    leaves the registers.  V^T fragments in that key order come from the
+//    row-major V tile through the gfx950 LDS transpose read
+//    (ds_read_b64_tr_b16: in each group of 16 lanes, lane 4r+q supplies four
+//    consecutive 16-bit values of row r and lane i receives column i of the
+//    four rows).
+//  * K and V tiles of 64 keys go from global memory straight into LDS
+//    (global_load_lds_dwordx4): three K buffers and two V buffers, one
+//    barrier per tile.  The compute runs in 32-key halves: the scores of the
+//    next half are formed on the MFMA pipe while the softmax of the current
+//    half is on the VALU, which needs K one tile ahead of V.
+//  * LDS rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads
+//    do not collide on banks.
+//  * exp is exp2 with scale*log2(e) folded into one FMA; l and acc are only
+//    rescaled when the running max grows by more than 2^8 (the result is
+//    unchanged up to rounding: numerator and denominator share the stale
+//    reference, and no weight exceeds 2^8); the row sum adds the fp32
+//    weights before they are rounded to bf16 for P V; LSE is converted back
+//    to the natural log at the end.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -50,298 +62,464 @@
 
 #include "attn_prefill.h"
 
+#define LDS_AS __attribute__((address_space(3)))
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 8;            // waves per workgroup
+constexpr int kWaves = 4;             // waves per workgroup, one per SIMD
 constexpr int kThreads = kWaves * 64;
-constexpr int kBC = 64;              // keys per K/V tile
+constexpr int kCols = 256;            // query columns (head, row) per workgroup
+constexpr int kBC = 64;               // keys per K/V tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kSlack = 8.0f;        // rescale only past 2^8 growth
 
-// Byte offset of (row, 16-byte chunk) in a swizzled K tile [kBC][D].
-template <int D>
-__device__ __forceinline__ int k_off(int j, int chunk) {
-  return j * (2 * D) + ((chunk ^ (j & 7)) << 4);
+// 16-byte chunk swizzles of the K and V tiles (row = key inside the tile).
+__device__ __forceinline__ int k_swz(int row) { return row & 7; }
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
+
+// max / sum of x over lanes l and l ^ 32
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Swizzle of V^T row t: differs for the 8 rows one 8-lane read group touches
-// and for the 8 rows (spaced by 8) one transposing write touches.
-__device__ __forceinline__ int vt_swz(int t) { return (t & 7) ^ ((t >> 3) & 7); }
-
-// Byte offset of (row t, 16-byte chunk) in a swizzled V^T tile [D][kBC].
-__device__ __forceinline__ int vt_off(int t, int chunk) {
-  return t * (2 * kBC) + ((chunk ^ vt_swz(t)) << 4);
+// Workgroup barrier that does not wait for outstanding memory operations
+// (the caller waits for exactly the loads the next tile needs); the signal
+// fences keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void tile_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Position of key j (0..63) of a tile inside a V^T row.  Inside each group
-// of 16 keys, bits 2 and 3 are swapped: this is the order in which the score
-// result's registers feed the P V contraction as a B operand.
-__device__ __forceinline__ int key_slot(int j) {
-  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
+// s_waitcnt with only a vector-memory count (expcnt and lgkmcnt at maximum)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Raw buffer resource over `bytes` bytes from `base`: loads at offsets past
+// the end return zeros (the hardware range check), so the last, partial
+// K/V tile needs no clamping.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
 
-template <int D, int HW>
+// One wave's share of a K or V tile load, global -> LDS: `loads` loads of
+// 1 KB, lane i of load s bringing the 16 bytes at source offset src[s]
+// (relative to row j0 of rows of `row_bytes`) to LDS byte dst + 1 KB s + 16 i.
+__device__ __forceinline__ void dma_tile(const unsigned short* base, const int* src, int loads,
+                                         int row_bytes, int j0, int L, unsigned char* dst_shared) {
+  LDS_AS unsigned char* dst = (LDS_AS unsigned char*)dst_shared;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      make_rsrc((const unsigned char*)base + (size_t)j0 * row_bytes, (unsigned)(L - j0) * row_bytes);
+#pragma unroll
+  for (int s = 0; s < loads; ++s)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + s * 1024), 16, src[s], 0,
+                                             0, 0);
+}
+
+template <int D, int HWG>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ out,
     float* __restrict__ lse, int L, int n_q, int n_kv, int n_qblk, int items_per_qblk,
     float scale, int causal) {
-  constexpr int BR = 32 * kWaves / HW;        // query rows per workgroup
-  constexpr int KT_BYTES = kBC * D * 2;       // K tile
-  constexpr int VT_BYTES = D * kBC * 2;       // V^T tile
-  constexpr int STAGE = KT_BYTES + VT_BYTES;
-  constexpr int KSTEPS = D / 16;              // k-steps of Q K^T
-  constexpr int TBLK = D / 32;                // 32-wide blocks of O^T rows
-  constexpr int KCHUNKS = D / 8;              // 16-byte chunks per K row
-  constexpr int K_LOADS = kBC * KCHUNKS / kThreads;  // K chunks per thread
-  constexpr int V_UNITS = (kBC / 2) * KCHUNKS;       // (row pair, chunk) units
+  constexpr int BR = kCols / HWG;              // query rows per workgroup
+  constexpr int KSTEPS = D / 16;               // k-steps of Q K^T
+  constexpr int TBLK = D / 32;                 // 32-row blocks of O^T
+  constexpr int ROWB = 2 * D;                  // bytes per K or V row
+  constexpr int TILE = kBC * ROWB;             // bytes per K or V tile
+  constexpr int LOADS = TILE / (kWaves * 1024);  // 1 KB loads per wave per tile
+  static_assert(LOADS * kWaves * 1024 == TILE, "tile must split into 1 KB loads");
+  constexpr int RING = 4;                      // tiles per ring
+  constexpr int VRING = 0;                     // V ring at [0, 4 TILE)
+  constexpr int KRING = RING * TILE;           // K ring at [4 TILE, 8 TILE)
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * RING * TILE];
+  LDS_AS unsigned char* const smem_l = (LDS_AS unsigned char*)smem;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int hi = lane >> 5;     // which half of the wave
-  const int col = lane & 31;    // query column inside the wave's 32 rows
+  const int col = lane & 31;    // query column inside a 32-column block
 
   // ---- work item: heavy q-blocks first; neighbouring ids differ in head
   const int item = blockIdx.x;
   const int qb = n_qblk - 1 - item / items_per_qblk;
   int rest = item % items_per_qblk;
   const int g = n_q / n_kv;
-  const int ngroups = g / HW;
+  const int ngroups = g / HWG;
   const int hg = rest % ngroups;
   rest /= ngroups;
   const int kvh = rest % n_kv;
   const int b = rest / n_kv;
 
-  const int h = kvh * g + hg * HW + (wave % HW);
-  const int q0 = qb * BR + (wave / HW) * 32;  // first row of this wave
-  const int qi = q0 + col;                    // this lane's query row
+  // the wave's two 32-column blocks: columns 32 (wave + 4 ib) of the
+  // workgroup, column c being head c / BR, row c % BR of the q-block
+  int hb[2], q0b[2];
+#pragma unroll
+  for (int ib = 0; ib < 2; ++ib) {
+    const int c0 = 32 * (wave + 4 * ib);
+    hb[ib] = kvh * g + hg * HWG + c0 / BR;
+    q0b[ib] = qb * BR + c0 % BR;
+  }
 
   const size_t L64 = (size_t)L;
-  const unsigned short* qrow = q + (((size_t)b * n_q + h) * L64 + (size_t)qi) * D;
   const unsigned short* kbase = k + ((size_t)b * n_kv + kvh) * L64 * D;
   const unsigned short* vbase = v + ((size_t)b * n_kv + kvh) * L64 * D;
 
-  // ---- tiles this workgroup streams, and the tiles this wave computes
-  const int wg_end = min(qb * BR + BR, L);  // one past the last valid row
+  // ---- tiles the workgroup streams, and tiles this wave computes
+  const int wg_end = min(qb * BR + BR, L);
   const int n_tiles = causal ? (wg_end + kBC - 1) / kBC : (L + kBC - 1) / kBC;
-  int wave_tiles = 0;
-  if (q0 < L) wave_tiles = causal ? (min(q0 + 31, L - 1) / kBC + 1) : n_tiles;
-
-  // ---- Q fragment, the B operand of S^T = K Q^T: Q[qi][16 kk + 8 hi + 0..7]
-  bf16x8 qf[KSTEPS];
+  int last_row = -1;
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (qi < L) raw = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hi * 8);
-    qf[kk] = __builtin_bit_cast(bf16x8, raw);
+  for (int ib = 0; ib < 2; ++ib)
+    if (q0b[ib] < L) last_row = max(last_row, min(q0b[ib] + 31, L - 1));
+  const int wave_tiles = last_row < 0 ? 0 : (causal ? last_row / kBC + 1 : n_tiles);
+
+  // ---- Q fragments (B operand of S^T = K Q^T): Q[row][16 kk + 8 hi + 0..7]
+  bf16x8 qf[2][KSTEPS];
+#pragma unroll
+  for (int ib = 0; ib < 2; ++ib) {
+    const int qi = q0b[ib] + col;
+    const unsigned short* qrow = q + (((size_t)b * n_q + hb[ib]) * L64 + (size_t)qi) * D;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (qi < L) raw = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hi * 8);
+      qf[ib][kk] = __builtin_bit_cast(bf16x8, raw);
+    }
   }
 
-  // ---- K/V tile staging: global -> registers -> LDS
-  u32x4 kreg[K_LOADS];
-  u32x4 vreg[2];
-  const int v_unit_ok = tid < V_UNITS;
-  const int v_pair = tid / KCHUNKS;   // rows 2 v_pair, 2 v_pair + 1
-  const int v_chunk = tid % KCHUNKS;  // columns 8 v_chunk .. + 7
-
-  auto load_tile = [&](int tile) {
-    const int j0 = tile * kBC;
+  // ---- tile loads, global -> LDS.  Load s of this wave fills LDS bytes
+  // [1 KB (wave * LOADS + s), +1 KB) of a tile; lane i fills 16 bytes at 16 i
+  // with the chunk the row's swizzle puts there.  These source offsets do not
+  // change from tile to tile.
+  int k_src[LOADS], v_src[LOADS];
 #pragma unroll
-    for (int s = 0; s < K_LOADS; ++s) {
-      const int id = tid + s * kThreads;
-      const int j = id / KCHUNKS, c = id % KCHUNKS;
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (j0 + j < L)
-        raw = *reinterpret_cast<const u32x4*>(kbase + (size_t)(j0 + j) * D + c * 8);
-      kreg[s] = raw;
-    }
-    if (v_unit_ok) {
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int j = j0 + 2 * v_pair + r;
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (j < L) raw = *reinterpret_cast<const u32x4*>(vbase + (size_t)j * D + v_chunk * 8);
-        vreg[r] = raw;
-      }
-    }
+  for (int s = 0; s < LOADS; ++s) {
+    const int byte = (wave * LOADS + s) * 1024 + lane * 16;
+    const int row = byte / ROWB;
+    const int pos = (byte % ROWB) >> 4;
+    k_src[s] = row * ROWB + ((pos ^ k_swz(row)) << 4);
+    v_src[s] = row * ROWB + ((pos ^ v_swz(row)) << 4);
+  }
+  auto load_tile = [&] __device__ (const unsigned short* base, const int (&src)[LOADS], int tile,
+                       int lds_off) __attribute__((always_inline)) {
+    dma_tile(base, src, LOADS, ROWB, tile * kBC, L, smem + lds_off + wave * LOADS * 1024);
   };
 
-  auto store_tile = [&](int buf) {
-    unsigned char* ks = smem + buf * STAGE;
-    unsigned char* vs = ks + KT_BYTES;
+  // ---- per-lane LDS read offsets
+  // K rows col (+32 jb), the A operand of S^T = K Q^T, k-step kk
+  int k_rd[KSTEPS];
 #pragma unroll
-    for (int s = 0; s < K_LOADS; ++s) {
-      const int id = tid + s * kThreads;
-      const int j = id / KCHUNKS, c = id % KCHUNKS;
-      *reinterpret_cast<u32x4*>(ks + k_off<D>(j, c)) = kreg[s];
-    }
-    if (v_unit_ok) {
-      // V rows j, j+1 (8 columns each) -> 8 V^T rows, one dword per row
-      // holding (V[j][t], V[j+1][t]).
-      const int j = 2 * v_pair;
-      const int slot = key_slot(j);
+  for (int kk = 0; kk < KSTEPS; ++kk)
+    k_rd[kk] = KRING + col * ROWB + (((2 * kk + hi) ^ k_swz(col)) << 4);
+  // V^T through ds_read_b64_tr_b16: lane 16G + 4r + qq reads V[key][t .. t+3],
+  // key = 16 ks + 8 u + 4 (G / 2) + r, t = 32 tb + 16 (G % 2) + 4 qq, and
+  // receives V^T[32 tb + lane % 32][keys]
+  int v_rd[TBLK];
+  {
+    const int tr_r = (lane >> 2) & 3;
+    const int tr_q = lane & 3;
+    const int tr_g = (lane >> 4) & 1;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const unsigned int w0 = vreg[0][e >> 1], w1 = vreg[1][e >> 1];
-        // low halves for even columns, high halves for odd ones
-        const unsigned int packed = (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
-                                            : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-        const int t = v_chunk * 8 + e;
-        *reinterpret_cast<unsigned int*>(vs + vt_off(t, slot >> 3) + (slot & 7) * 2) = packed;
-      }
+    for (int tb = 0; tb < TBLK; ++tb) {
+      const int t = 32 * tb + 16 * tr_g + 4 * tr_q;
+      const int key = 4 * hi + tr_r;  // plus 16 ks + 8 u, which keep key & 3
+      v_rd[tb] = VRING + key * ROWB + (((t >> 3) ^ v_swz(key)) << 4) + ((t >> 2) & 1) * 8;
     }
-  };
+  }
 
-  // ---- running state (log2 domain, scaled): m, lane-partial row sum, acc
-  f32x16 acc[TBLK];
+  // ---- running state per block: reference max m (log2 domain), lane
+  // partial row sum l, accumulator O^T
+  f32x16 acc[2][TBLK];
 #pragma unroll
-  for (int tb = 0; tb < TBLK; ++tb)
+  for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[tb][r] = 0.0f;
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
-  const float c2 = scale * kLog2e;   // score -> log2 domain
+    for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[ib][tb][r] = 0.0f;
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.0f, 0.0f};
+  const float c2 = scale * kLog2e;
   const bool fast_scale = c2 > 0.0f;
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < n_tiles) load_tile(tile + 1);
-    __syncthreads();
-
-    if (tile < wave_tiles) {
-      const unsigned char* ks = smem + buf * STAGE;
-      const unsigned char* vs = ks + KT_BYTES;
-      const int j0 = tile * kBC;
-
-      // S^T = K Q^T for the tile's two 32-key blocks
-      f32x16 s[2];
+  // K fragments of ring slot `slot`, keys 32 jb .. 32 jb + 31
+  auto load_kfrags = [&] __device__ (bf16x8 (&kf)[KSTEPS], int slot, int jb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      kf[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(smem_l + k_rd[kk] + slot * TILE +
+                                                       jb * 32 * ROWB);
+  };
+  // V^T fragments of ring slot `slot`, k-steps 2 jb and 2 jb + 1
+  auto load_vfrags = [&] __device__ (bf16x8 (&vf)[TBLK][2], int slot, int jb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[jb][r] = 0.0f;
-        const int j = jb * 32 + col;
+    for (int tb = 0; tb < TBLK; ++tb)
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + k_off<D>(j, 2 * kk + hi));
-          s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[jb], 0, 0, 0);
-        }
+      for (int h = 0; h < 2; ++h) {
+        const LDS_AS unsigned char* base =
+            smem_l + v_rd[tb] + slot * TILE + (2 * jb + h) * 16 * ROWB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base));
+        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base + 8 * ROWB));
+        vf[tb][h] = __builtin_bit_cast(
+            bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                            __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]});
       }
+  };
 
-      // mask: keys after the query (causal) and keys past the end
-      const bool need_mask = (causal && j0 + kBC - 1 > q0) || (j0 + kBC > L);
-      float c = c2;
-      if (need_mask || !fast_scale) {
+  // S^T = K Q^T for both blocks; each K fragment feeds two MFMAs
+  auto qk_mfma = [&] __device__ (f32x16 (&S)[2], const bf16x8 (&kf)[KSTEPS]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+    for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = j0 + jb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-            const bool dead = (causal && j > qi) || j >= L;
-            s[jb][r] = dead ? -INFINITY : s[jb][r] * c2;
-          }
-        c = 1.0f;
+      for (int r = 0; r < 16; ++r) S[ib][r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[0][kk], S[0], 0, 0, 0);
+      S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[1][kk], S[1], 0, 0, 0);
+    }
+  };
+
+  // O^T += V^T P^T for one block (the TBLK accumulators interleave, so no
+  // MFMA waits on the one just issued)
+  auto pv_mfma = [&] __device__ (const bf16x8 (&vf)[TBLK][2], const bf16x8 (&pk)[2], int ib) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int tb = 0; tb < TBLK; ++tb)
+        acc[ib][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[tb][h], pk[h], acc[ib][tb], 0, 0, 0);
+  };
+
+  // row max of one block's 32 scores per lane pair (branch-free)
+  auto row_max = [&] __device__ (const f32x16& s) __attribute__((always_inline)) {
+    float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    return pair_max(mx);
+  };
+
+  // softmax, first part, for the scores of keys j0 .. j0+31 (may branch):
+  // where the half straddles the diagonal or the end of the sequence, or the
+  // scale is not positive, mask and pre-scale the scores and retake the row
+  // max; then move the reference max (rescaling l and acc) only when the
+  // tile max exceeds it by more than 2^8.  Returns the multiplier and -m.
+  auto prepare = [&] __device__ (f32x16& s, float mx, int ib, int j0, float& c_out,
+                                 float& mneg_out) __attribute__((always_inline)) {
+    const int q0 = q0b[ib];
+    const int qi = q0 + col;
+    const bool need_mask = (causal && j0 + 31 > q0) || (j0 + 32 > L);
+    float c = c2;
+    if (need_mask || !fast_scale) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + (r >> 2) * 8 + hi * 4 + (r & 3);
+        const bool dead = (causal && j > qi) || j >= L;
+        s[r] = dead ? -INFINITY : s[r] * c2;
       }
-
-      // tile max of this lane's 32 scores, then across lanes l and l^32
-      float mx = s[0][0];
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run, mx * c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-
-      // p = 2^(c s - m); P^T in bf16 as the B operand of the P V k-steps
-      bf16x8 pk[4];
-      float psum = 0.0f;
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8 frag;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][half * 8 + e], c, -m_new));
-            psum += p;
-            frag[e] = (__bf16)p;
-          }
-          pk[jb * 2 + half] = frag;
-        }
-      l_run = l_run * alpha + psum;
-
+      c = 1.0f;
+      mx = row_max(s);
+    }
+    const float m_cand = mx * c;
+    if (__builtin_amdgcn_ballot_w64(m_cand > m_run[ib] + kSlack) != 0) {
+      const float m_new = fmaxf(m_run[ib], m_cand);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[ib] - m_new);
+      m_run[ib] = m_new;
+      l_run[ib] *= alpha;
 #pragma unroll
       for (int tb = 0; tb < TBLK; ++tb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[tb][r] *= alpha;
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int tb = 0; tb < TBLK; ++tb) {
-        const int t = tb * 32 + col;
-#pragma unroll
-        for (int ks4 = 0; ks4 < 4; ++ks4) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + vt_off(t, 2 * ks4 + hi));
-          acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[ks4], acc[tb], 0, 0, 0);
-        }
-      }
+        for (int r = 0; r < 16; ++r) acc[ib][tb][r] *= alpha;
     }
+    c_out = c;
+    mneg_out = -m_run[ib];
+  };
 
-    if (tile + 1 < n_tiles) store_tile(buf ^ 1);
+  // softmax, second part (branch-free): p = 2^(c s - m), the fp32 row sum,
+  // and P^T rounded to bf16 as two B-operand fragments
+  auto expo = [&] __device__ (const f32x16& s, int ib, float c, float mneg, bf16x8 (&pk)[2])
+      __attribute__((always_inline)) {
+    float psum = 0.0f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      bf16x8 frag;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[half * 8 + e], c, mneg));
+        psum += p;
+        frag[e] = (__bf16)p;
+      }
+      pk[half] = frag;
+    }
+    l_run[ib] += psum;
+  };
+
+  // Software pipeline over 32-key half-steps h = 2 t + jb.  Entering the
+  // region of half h: the scores of h are prepared (multiplier, -m), the K
+  // fragments of half h+1 and the V^T fragments of half h are in registers.
+  // The region (branch-free) forms the scores of h+1 on the MFMA pipe next
+  // to the exponentials of block 0 of h on the VALU, then P V of block 0
+  // next to the exponentials of block 1, then P V of block 1 next to the
+  // row max of h+1, and meanwhile reads the K fragments of h+2 and the V^T
+  // fragments of h+1 from LDS.  Only the mask and rescale decisions for h+1
+  // (rarely taken branches) sit between regions.  Past the wave's last half
+  // the region computes on stale LDS data whose results are never used.
+  struct Half {
+    f32x16 s[2];
+    bf16x8 kf[KSTEPS];
+    bf16x8 vf[TBLK][2];
+  };
+  Half hA, hB;
+  float cc[2], mn[2];   // multiplier and -m of the half being retired
+
+  auto region = [&] __device__ (int t, int ts, int jb, Half& cur, Half& nxt)
+      __attribute__((always_inline)) {
+    // ring slots and key halves of h+1 and h+2
+    const int slot1 = jb == 0 ? ts : (ts + 1) & (RING - 1);
+    const int jb1 = jb ^ 1;
+    const int slot2 = (ts + 1) & (RING - 1);
+    const int jb2 = jb;
+    load_kfrags(nxt.kf, slot2, jb2);
+    load_vfrags(nxt.vf, slot1, jb1);
+    qk_mfma(nxt.s, cur.kf);
+    bf16x8 p0[2], p1[2];
+    expo(cur.s[0], 0, cc[0], mn[0], p0);
+    pv_mfma(cur.vf, p0, 0);
+    expo(cur.s[1], 1, cc[1], mn[1], p1);
+    pv_mfma(cur.vf, p1, 1);
+    const float mx0 = row_max(nxt.s[0]);
+    const float mx1 = row_max(nxt.s[1]);
+    // pin the interleave:
+    //   16 x (1 QK MFMA, 4 VALU, 1 LDS read)
+    //    8 x (1 P V MFMA, 7 VALU, 1 LDS read)
+    //    8 x (1 P V MFMA, 5 VALU)
+#pragma unroll
+    for (int i = 0; i < 2 * KSTEPS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * TBLK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * TBLK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    // first softmax part of h+1 (keys of tile t + jb, half jb1)
+    const int j0n = (t + jb) * kBC + jb1 * 32;
+    prepare(nxt.s[0], mx0, 0, j0n, cc[0], mn[0]);
+    prepare(nxt.s[1], mx1, 1, j0n, cc[1], mn[1]);
+  };
+
+  // ---- prologue: K0..K2 and V0..V2 into LDS; scores of half 0 prepared,
+  // K fragments of half 1 and V^T fragments of half 0 in registers
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+    if (i < n_tiles) {
+      load_tile(kbase, k_src, i, KRING + i * TILE);
+      load_tile(vbase, v_src, i, VRING + i * TILE);
+    }
+  wait_vmcnt<0>();
+  tile_barrier();
+  if (wave_tiles > 0) {
+    load_kfrags(hB.kf, 0, 0);
+    qk_mfma(hA.s, hB.kf);
+    load_kfrags(hA.kf, 0, 1);
+    load_vfrags(hA.vf, 0, 0);
+    prepare(hA.s[0], row_max(hA.s[0]), 0, 0, cc[0], mn[0]);
+    prepare(hA.s[1], row_max(hA.s[1]), 1, 0, cc[1], mn[1]);
+  }
+
+  // one tile t (ring slot TS = t % 4, a constant once inlined): the loads of
+  // V(t+3) and K(t+3) fly during this tile and the next two; at its end the
+  // loads issued during the previous tile (V(t+2), K(t+2)) must have landed
+  auto tile_step = [&] __device__ (int TS, int t) __attribute__((always_inline)) {
+    const bool more = t + 3 < n_tiles;
+    if (more) {
+      load_tile(vbase, v_src, t + 3, VRING + ((TS + 3) & (RING - 1)) * TILE);
+      load_tile(kbase, k_src, t + 3, KRING + ((TS + 3) & (RING - 1)) * TILE);
+    }
+    if (t < wave_tiles) {
+      region(t, TS, 0, hA, hB);
+      region(t, TS, 1, hB, hA);
+    }
+    if (more)
+      wait_vmcnt<2 * LOADS>();
+    else
+      wait_vmcnt<0>();
+    tile_barrier();
+  };
+  for (int t = 0; t < n_tiles; t += RING) {
+    tile_step(0, t);
+    if (t + 1 < n_tiles) tile_step(1, t + 1);
+    if (t + 2 < n_tiles) tile_step(2, t + 2);
+    if (t + 3 < n_tiles) tile_step(3, t + 3);
   }
 
   // ---- epilogue: O = acc / l in bf16, LSE = ln 2 * (m + log2 l)
-  if (wave_tiles == 0 || qi >= L) return;
-  const float l_tot = l_run + xor32(l_run);
-  const float inv = 1.0f / l_tot;
-  unsigned short* orow = out + (((size_t)b * n_q + h) * L64 + (size_t)qi) * D;
 #pragma unroll
-  for (int tb = 0; tb < TBLK; ++tb)
+  for (int ib = 0; ib < 2; ++ib) {
+    const float l_tot = pair_sum(l_run[ib]);
+    const int qi = q0b[ib] + col;
+    if (wave_tiles == 0 || qi >= L) continue;
+    const float inv = 1.0f / l_tot;
+    unsigned short* orow = out + (((size_t)b * n_q + hb[ib]) * L64 + (size_t)qi) * D;
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const int t0 = tb * 32 + grp * 8 + hi * 4;
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      bf16x4 o4;
+    for (int tb = 0; tb < TBLK; ++tb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[tb][grp * 4 + e] * inv);
-      *reinterpret_cast<u32x2*>(orow + t0) = __builtin_bit_cast(u32x2, o4);
-    }
-  if (hi == 0)
-    lse[((size_t)b * n_q + h) * L64 + (size_t)qi] = (m_run + __log2f(l_tot)) * kLn2;
+      for (int grp = 0; grp < 4; ++grp) {
+        const int t0 = tb * 32 + grp * 8 + hi * 4;
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[ib][tb][grp * 4 + e] * inv);
+        *reinterpret_cast<u32x2*>(orow + t0) = __builtin_bit_cast(u32x2, o4);
+      }
+    if (hi == 0)
+      lse[((size_t)b * n_q + hb[ib]) * L64 + (size_t)qi] = (m_run[ib] + __log2f(l_tot)) * kLn2;
+  }
 }
 
 // Heads per workgroup: the largest of 8, 4, 2, 1 that divides g.
-int pick_hw(int g) {
+int pick_hwg(int g) {
   if (g % 8 == 0) return 8;
   if (g % 4 == 0) return 4;
   if (g % 2 == 0) return 2;
   return 1;
 }
 
-template <int D, int HW>
+template <int D, int HWG>
 int launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int L,
            int n_q, int n_kv, float scale, int causal, hipStream_t stream) {
-  constexpr int BR = 32 * kWaves / HW;
+  constexpr int BR = kCols / HWG;
   const int n_qblk = (L + BR - 1) / BR;
-  const long long items_per_qblk = (long long)B * n_kv * ((n_q / n_kv) / HW);
+  const long long items_per_qblk = (long long)B * n_kv * ((n_q / n_kv) / HWG);
   const long long grid = items_per_qblk * n_qblk;
   if (items_per_qblk > INT_MAX || grid > INT_MAX) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, HW>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, HWG>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                      static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
                      static_cast<const unsigned short*>(v), static_cast<unsigned short*>(out), lse,
                      L, n_q, n_kv, n_qblk, (int)items_per_qblk, scale, causal);
@@ -351,7 +529,7 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, i
 template <int D>
 int launch_d(const void* q, const void* k, const void* v, void* out, float* lse, int B, int L,
              int n_q, int n_kv, float scale, int causal, hipStream_t stream) {
-  switch (pick_hw(n_q / n_kv)) {
+  switch (pick_hwg(n_q / n_kv)) {
     case 8: return launch<D, 8>(q, k, v, out, lse, B, L, n_q, n_kv, scale, causal, stream);
     case 4: return launch<D, 4>(q, k, v, out, lse, B, L, n_q, n_kv, scale, causal, stream);
     case 2: return launch<D, 2>(q, k, v, out, lse, B, L, n_q, n_kv, scale, causal, stream);
