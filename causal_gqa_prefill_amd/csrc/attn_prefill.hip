@@ -47,7 +47,7 @@
 //    next half are formed on the MFMA pipe while the softmax of the current
 //    half is on the VALU, which needs K one tile ahead of V.
 //  * LDS rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads
-//    do not collide on banks.
+//    do not collide on banks (see k_swz / v_swz).
 //  * exp is exp2 with scale*log2(e) folded into one FMA; l and acc are only
 //    rescaled when the running max grows by more than 2^8 (the result is
 //    unchanged up to rounding: numerator and denominator share the stale
@@ -83,8 +83,22 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;        // rescale only past 2^8 growth
 
 // 16-byte chunk swizzles of the K and V tiles (row = key inside the tile).
-__device__ __forceinline__ int k_swz(int row) { return row & 7; }
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
+// gfx950's LDS has 64 four-byte banks and serves 16 lanes of a 16-byte read
+// or 32 lanes of an 8-byte read per cycle (measured: conflict counters are
+// zero for contiguous reads).  K: the 16 lanes of a 16-byte read take 16
+// consecutive rows at one chunk, so the chunk is XORed with the row's low
+// bits to land on 16 distinct 16-byte slots of a 256-byte bank window.  V:
+// the 32 lanes of a transpose read take 4 rows x 2 chunk pairs; XORing the
+// chunk with 4 (row & 3) (d_h = 128) puts the 8 32-byte pieces on distinct
+// slots.  For d_h = 64 two rows share a 256-byte window, hence the shifts.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
 
 // max / sum of x over lanes l and l ^ 32
 __device__ __forceinline__ float pair_max(float x) {
@@ -125,11 +139,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 // One wave's share of a K or V tile load, global -> LDS: `loads` loads of
 // 1 KB, lane i of load s bringing the 16 bytes at source offset src[s]
 // (relative to row j0 of rows of `row_bytes`) to LDS byte dst + 1 KB s + 16 i.
+// A tile at or past row L reads as zeros and touches no memory.
 __device__ __forceinline__ void dma_tile(const unsigned short* base, const int* src, int loads,
                                          int row_bytes, int j0, int L, unsigned char* dst_shared) {
   LDS_AS unsigned char* dst = (LDS_AS unsigned char*)dst_shared;
   const __amdgpu_buffer_rsrc_t rsrc =
-      make_rsrc((const unsigned char*)base + (size_t)j0 * row_bytes, (unsigned)(L - j0) * row_bytes);
+      make_rsrc((const unsigned char*)base + (size_t)j0 * row_bytes,
+                (unsigned)max(L - j0, 0) * row_bytes);
 #pragma unroll
   for (int s = 0; s < loads; ++s)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + s * 1024), 16, src[s], 0,
@@ -220,8 +236,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const int byte = (wave * LOADS + s) * 1024 + lane * 16;
     const int row = byte / ROWB;
     const int pos = (byte % ROWB) >> 4;
-    k_src[s] = row * ROWB + ((pos ^ k_swz(row)) << 4);
-    v_src[s] = row * ROWB + ((pos ^ v_swz(row)) << 4);
+    k_src[s] = row * ROWB + ((pos ^ k_swz<D>(row)) << 4);
+    v_src[s] = row * ROWB + ((pos ^ v_swz<D>(row)) << 4);
   }
   auto load_tile = [&] __device__ (const unsigned short* base, const int (&src)[LOADS], int tile,
                        int lds_off) __attribute__((always_inline)) {
@@ -233,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   int k_rd[KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk)
-    k_rd[kk] = KRING + col * ROWB + (((2 * kk + hi) ^ k_swz(col)) << 4);
+    k_rd[kk] = KRING + col * ROWB + (((2 * kk + hi) ^ k_swz<D>(col)) << 4);
   // V^T through ds_read_b64_tr_b16: lane 16G + 4r + qq reads V[key][t .. t+3],
   // key = 16 ks + 8 u + 4 (G / 2) + r, t = 32 tb + 16 (G % 2) + 4 qq, and
   // receives V^T[32 tb + lane % 32][keys]
@@ -245,8 +261,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
 #pragma unroll
     for (int tb = 0; tb < TBLK; ++tb) {
       const int t = 32 * tb + 16 * tr_g + 4 * tr_q;
-      const int key = 4 * hi + tr_r;  // plus 16 ks + 8 u, which keep key & 3
-      v_rd[tb] = VRING + key * ROWB + (((t >> 3) ^ v_swz(key)) << 4) + ((t >> 2) & 1) * 8;
+      const int key = 4 * hi + tr_r;  // plus 16 ks + 8 u, which keep the swizzle
+      v_rd[tb] = VRING + key * ROWB + (((t >> 3) ^ v_swz<D>(key)) << 4) + ((t >> 2) & 1) * 8;
     }
   }
 
@@ -287,14 +303,18 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
       }
   };
 
-  // S^T = K Q^T for both blocks; each K fragment feeds two MFMAs
-  auto qk_mfma = [&] __device__ (f32x16 (&S)[2], const bf16x8 (&kf)[KSTEPS]) __attribute__((always_inline)) {
+  // S^T = K Q^T for both blocks, k-steps [k0, k1); each K fragment feeds
+  // two MFMAs.  k0 = 0 starts from zero.
+  auto qk_mfma = [&] __device__ (f32x16 (&S)[2], const bf16x8 (&kf)[KSTEPS], int k0, int k1)
+      __attribute__((always_inline)) {
+    if (k0 == 0) {
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
+      for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[ib][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) S[ib][r] = 0.0f;
+    }
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
+    for (int kk = k0; kk < k1; ++kk) {
       S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[0][kk], S[0], 0, 0, 0);
       S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[1][kk], S[1], 0, 0, 0);
     }
@@ -374,22 +394,30 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   };
 
   // Software pipeline over 32-key half-steps h = 2 t + jb.  Entering the
-  // region of half h: the scores of h are prepared (multiplier, -m), the K
-  // fragments of half h+1 and the V^T fragments of half h are in registers.
-  // The region (branch-free) forms the scores of h+1 on the MFMA pipe next
-  // to the exponentials of block 0 of h on the VALU, then P V of block 0
-  // next to the exponentials of block 1, then P V of block 1 next to the
-  // row max of h+1, and meanwhile reads the K fragments of h+2 and the V^T
-  // fragments of h+1 from LDS.  Only the mask and rescale decisions for h+1
-  // (rarely taken branches) sit between regions.  Past the wave's last half
-  // the region computes on stale LDS data whose results are never used.
+  // region of half h: the raw scores of h and their row max are in
+  // registers, as are the K fragments of half h+1 and the V^T fragments of
+  // half h.  The region first puts a few QK^T MFMAs of h+1 on the pipe (they
+  // need nothing from the softmax) and, in the first half of a tile, issues
+  // the tile loads; while those run it takes the first softmax part of h
+  // (mask and rescale decisions, rarely taken branches).  Then, branch-free:
+  // the rest of the scores of h+1 next to the exponentials of block 0 of h,
+  // P V of block 0 next to the exponentials of block 1, P V of block 1 next
+  // to the row max of h+1, with the K fragments of h+2 and the V^T fragments
+  // of h+1 read from LDS meanwhile.  Past the wave's last half the region
+  // computes on stale LDS data whose results are never used.
   struct Half {
     f32x16 s[2];
     bf16x8 kf[KSTEPS];
     bf16x8 vf[TBLK][2];
   };
   Half hA, hB;
-  float cc[2], mn[2];   // multiplier and -m of the half being retired
+  float mx[2];          // row max of the raw scores of the half being retired
+  constexpr int KA = 2; // k-steps of h+1 issued ahead of the softmax branches
+
+  auto issue_tile_loads = [&] __device__ (int TS, int t) __attribute__((always_inline)) {
+    load_tile(vbase, v_src, t + 3, VRING + ((TS + 3) & (RING - 1)) * TILE);
+    load_tile(kbase, k_src, t + 3, KRING + ((TS + 3) & (RING - 1)) * TILE);
+  };
 
   auto region = [&] __device__ (int t, int ts, int jb, Half& cur, Half& nxt)
       __attribute__((always_inline)) {
@@ -398,79 +426,54 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const int jb1 = jb ^ 1;
     const int slot2 = (ts + 1) & (RING - 1);
     const int jb2 = jb;
+    qk_mfma(nxt.s, cur.kf, 0, KA);
+    if (jb == 0) issue_tile_loads(ts, t);
+    float cc[2], mn[2];
+    const int j0 = t * kBC + jb * 32;
+    prepare(cur.s[0], mx[0], 0, j0, cc[0], mn[0]);
+    prepare(cur.s[1], mx[1], 1, j0, cc[1], mn[1]);
     load_kfrags(nxt.kf, slot2, jb2);
     load_vfrags(nxt.vf, slot1, jb1);
-    qk_mfma(nxt.s, cur.kf);
+    qk_mfma(nxt.s, cur.kf, KA, KSTEPS);
     bf16x8 p0[2], p1[2];
     expo(cur.s[0], 0, cc[0], mn[0], p0);
     pv_mfma(cur.vf, p0, 0);
     expo(cur.s[1], 1, cc[1], mn[1], p1);
     pv_mfma(cur.vf, p1, 1);
-    const float mx0 = row_max(nxt.s[0]);
-    const float mx1 = row_max(nxt.s[1]);
-    // pin the interleave:
-    //   16 x (1 QK MFMA, 4 VALU, 1 LDS read)
-    //    8 x (1 P V MFMA, 7 VALU, 1 LDS read)
-    //    8 x (1 P V MFMA, 5 VALU)
-#pragma unroll
-    for (int i = 0; i < 2 * KSTEPS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 2 * TBLK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 2 * TBLK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    }
-    // first softmax part of h+1 (keys of tile t + jb, half jb1)
-    const int j0n = (t + jb) * kBC + jb1 * 32;
-    prepare(nxt.s[0], mx0, 0, j0n, cc[0], mn[0]);
-    prepare(nxt.s[1], mx1, 1, j0n, cc[1], mn[1]);
+    mx[0] = row_max(nxt.s[0]);
+    mx[1] = row_max(nxt.s[1]);
   };
 
-  // ---- prologue: K0..K2 and V0..V2 into LDS; scores of half 0 prepared,
-  // K fragments of half 1 and V^T fragments of half 0 in registers
+  // ---- prologue: K0..K2 and V0..V2 into LDS; raw scores of half 0 and
+  // their max, K fragments of half 1 and V^T fragments of half 0 in registers
 #pragma unroll
-  for (int i = 0; i < 3; ++i)
-    if (i < n_tiles) {
-      load_tile(kbase, k_src, i, KRING + i * TILE);
-      load_tile(vbase, v_src, i, VRING + i * TILE);
-    }
+  for (int i = 0; i < 3; ++i) {
+    load_tile(kbase, k_src, i, KRING + i * TILE);
+    load_tile(vbase, v_src, i, VRING + i * TILE);
+  }
   wait_vmcnt<0>();
   tile_barrier();
   if (wave_tiles > 0) {
     load_kfrags(hB.kf, 0, 0);
-    qk_mfma(hA.s, hB.kf);
+    qk_mfma(hA.s, hB.kf, 0, KSTEPS);
     load_kfrags(hA.kf, 0, 1);
     load_vfrags(hA.vf, 0, 0);
-    prepare(hA.s[0], row_max(hA.s[0]), 0, 0, cc[0], mn[0]);
-    prepare(hA.s[1], row_max(hA.s[1]), 1, 0, cc[1], mn[1]);
+    mx[0] = row_max(hA.s[0]);
+    mx[1] = row_max(hA.s[1]);
   }
 
   // one tile t (ring slot TS = t % 4, a constant once inlined): the loads of
-  // V(t+3) and K(t+3) fly during this tile and the next two; at its end the
-  // loads issued during the previous tile (V(t+2), K(t+2)) must have landed
+  // V(t+3) and K(t+3) (zeros past the end) fly during this tile and the next
+  // two; at its end the loads issued during the previous tile must have
+  // landed
   auto tile_step = [&] __device__ (int TS, int t) __attribute__((always_inline)) {
-    const bool more = t + 3 < n_tiles;
-    if (more) {
-      load_tile(vbase, v_src, t + 3, VRING + ((TS + 3) & (RING - 1)) * TILE);
-      load_tile(kbase, k_src, t + 3, KRING + ((TS + 3) & (RING - 1)) * TILE);
-    }
     if (t < wave_tiles) {
       region(t, TS, 0, hA, hB);
       region(t, TS, 1, hB, hA);
+    } else {
+      issue_tile_loads(TS, t);
     }
-    if (more)
-      wait_vmcnt<2 * LOADS>();
-    else
-      wait_vmcnt<0>();
+    wait_vmcnt<2 * LOADS>();
     tile_barrier();
   };
   for (int t = 0; t < n_tiles; t += RING) {
@@ -479,6 +482,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     if (t + 2 < n_tiles) tile_step(2, t + 2);
     if (t + 3 < n_tiles) tile_step(3, t + 3);
   }
+  wait_vmcnt<0>();   // no tile load may still be writing LDS when the wave ends
 
   // ---- epilogue: O = acc / l in bf16, LSE = ln 2 * (m + log2 l)
 #pragma unroll
