@@ -21,11 +21,15 @@
 //    ("flops / prefill-attention", section "Arithmetic intensity").
 //
 // CDNA4 mapping:
-//  * A workgroup is 4 wave64s, one per SIMD, covering 256 query columns:
-//    HWG heads of one group times BR = 256 / HWG rows.  Each wave owns two
-//    blocks of 32 columns, so every K or V operand fragment it reads from LDS
-//    feeds two MFMAs (LDS delivers 128 B/clk/CU; one fragment per MFMA would
-//    use all of it at the MFMA peak).
+//  * A workgroup covers 256 query columns: HWG heads of one group times
+//    BR = 256 / HWG rows.  By default it is 8 wave64s, two per SIMD, each
+//    owning one block of 32 columns: the two waves of a SIMD cover each
+//    other's latencies, and at d_h = 128 one wave's softmax work nearly fills
+//    the issue slots next to its own MFMAs, so a lone wave per SIMD stalls.
+//    Each K or V^T fragment read from LDS feeds one MFMA per block; the LDS
+//    (measured ~250 B/clk/CU for 16-byte reads) has room for that.  The
+//    kernel is also written for two blocks per wave (4 waves, one per SIMD,
+//    each fragment feeding two MFMAs), selectable at build time.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand, Q (held in
 //    VGPRs for the whole loop) the B operand.  In the 32x32 result lane l
@@ -74,8 +78,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;             // waves per workgroup, one per SIMD
-constexpr int kThreads = kWaves * 64;
+#ifndef ATTN_BLOCKS_PER_WAVE
+#define ATTN_BLOCKS_PER_WAVE 1
+#endif
+// 32-column blocks per wave: 2 (4 waves, one per SIMD) or 1 (8 waves, two
+// per SIMD); a workgroup always covers kCols query columns
+constexpr int kBlocksPerWave = ATTN_BLOCKS_PER_WAVE;
 constexpr int kCols = 256;            // query columns (head, row) per workgroup
 constexpr int kBC = 64;               // keys per K/V tile
 constexpr float kLog2e = 1.4426950408889634f;
@@ -152,19 +160,20 @@ __device__ __forceinline__ void dma_tile(const unsigned short* base, const int* 
                                              0, 0);
 }
 
-template <int D, int HWG>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
+template <int D, int HWG, int NB>
+__global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ out,
     float* __restrict__ lse, int L, int n_q, int n_kv, int n_qblk, int items_per_qblk,
     float scale, int causal) {
+  constexpr int NW = kCols / (32 * NB);        // waves per workgroup
   constexpr int BR = kCols / HWG;              // query rows per workgroup
   constexpr int KSTEPS = D / 16;               // k-steps of Q K^T
   constexpr int TBLK = D / 32;                 // 32-row blocks of O^T
   constexpr int ROWB = 2 * D;                  // bytes per K or V row
   constexpr int TILE = kBC * ROWB;             // bytes per K or V tile
-  constexpr int LOADS = TILE / (kWaves * 1024);  // 1 KB loads per wave per tile
-  static_assert(LOADS * kWaves * 1024 == TILE, "tile must split into 1 KB loads");
+  constexpr int LOADS = TILE / (NW * 1024);    // 1 KB loads per wave per tile
+  static_assert(LOADS * NW * 1024 == TILE, "tile must split into 1 KB loads");
   constexpr int RING = 4;                      // tiles per ring
   constexpr int VRING = 0;                     // V ring at [0, 4 TILE)
   constexpr int KRING = RING * TILE;           // K ring at [4 TILE, 8 TILE)
@@ -189,12 +198,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   const int kvh = rest % n_kv;
   const int b = rest / n_kv;
 
-  // the wave's two 32-column blocks: columns 32 (wave + 4 ib) of the
+  // the wave's NB 32-column blocks: columns 32 (wave + NW ib) of the
   // workgroup, column c being head c / BR, row c % BR of the q-block
-  int hb[2], q0b[2];
+  int hb[NB], q0b[NB];
 #pragma unroll
-  for (int ib = 0; ib < 2; ++ib) {
-    const int c0 = 32 * (wave + 4 * ib);
+  for (int ib = 0; ib < NB; ++ib) {
+    const int c0 = 32 * (wave + NW * ib);
     hb[ib] = kvh * g + hg * HWG + c0 / BR;
     q0b[ib] = qb * BR + c0 % BR;
   }
@@ -208,14 +217,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   const int n_tiles = causal ? (wg_end + kBC - 1) / kBC : (L + kBC - 1) / kBC;
   int last_row = -1;
 #pragma unroll
-  for (int ib = 0; ib < 2; ++ib)
+  for (int ib = 0; ib < NB; ++ib)
     if (q0b[ib] < L) last_row = max(last_row, min(q0b[ib] + 31, L - 1));
   const int wave_tiles = last_row < 0 ? 0 : (causal ? last_row / kBC + 1 : n_tiles);
 
   // ---- Q fragments (B operand of S^T = K Q^T): Q[row][16 kk + 8 hi + 0..7]
-  bf16x8 qf[2][KSTEPS];
+  bf16x8 qf[NB][KSTEPS];
 #pragma unroll
-  for (int ib = 0; ib < 2; ++ib) {
+  for (int ib = 0; ib < NB; ++ib) {
     const int qi = q0b[ib] + col;
     const unsigned short* qrow = q + (((size_t)b * n_q + hb[ib]) * L64 + (size_t)qi) * D;
 #pragma unroll
@@ -268,15 +277,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
 
   // ---- running state per block: reference max m (log2 domain), lane
   // partial row sum l, accumulator O^T
-  f32x16 acc[2][TBLK];
+  f32x16 acc[NB][TBLK];
 #pragma unroll
-  for (int ib = 0; ib < 2; ++ib)
+  for (int ib = 0; ib < NB; ++ib)
 #pragma unroll
     for (int tb = 0; tb < TBLK; ++tb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[ib][tb][r] = 0.0f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.0f, 0.0f};
+  float m_run[NB], l_run[NB];
+#pragma unroll
+  for (int ib = 0; ib < NB; ++ib) {
+    m_run[ib] = -INFINITY;
+    l_run[ib] = 0.0f;
+  }
   const float c2 = scale * kLog2e;
   const bool fast_scale = c2 > 0.0f;
 
@@ -303,21 +316,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
       }
   };
 
-  // S^T = K Q^T for both blocks, k-steps [k0, k1); each K fragment feeds
-  // two MFMAs.  k0 = 0 starts from zero.
-  auto qk_mfma = [&] __device__ (f32x16 (&S)[2], const bf16x8 (&kf)[KSTEPS], int k0, int k1)
+  // S^T = K Q^T for the wave's blocks, k-steps [k0, k1); each K fragment
+  // feeds NB MFMAs.  k0 = 0 starts from zero.
+  auto qk_mfma = [&] __device__ (f32x16 (&S)[NB], const bf16x8 (&kf)[KSTEPS], int k0, int k1)
       __attribute__((always_inline)) {
     if (k0 == 0) {
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
+      for (int ib = 0; ib < NB; ++ib)
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[ib][r] = 0.0f;
     }
 #pragma unroll
-    for (int kk = k0; kk < k1; ++kk) {
-      S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[0][kk], S[0], 0, 0, 0);
-      S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[1][kk], S[1], 0, 0, 0);
-    }
+    for (int kk = k0; kk < k1; ++kk)
+#pragma unroll
+      for (int ib = 0; ib < NB; ++ib)
+        S[ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[ib][kk], S[ib], 0, 0, 0);
   };
 
   // O^T += V^T P^T for one block (the TBLK accumulators interleave, so no
@@ -394,25 +407,23 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   };
 
   // Software pipeline over 32-key half-steps h = 2 t + jb.  Entering the
-  // region of half h: the raw scores of h and their row max are in
-  // registers, as are the K fragments of half h+1 and the V^T fragments of
-  // half h.  The region first puts a few QK^T MFMAs of h+1 on the pipe (they
-  // need nothing from the softmax) and, in the first half of a tile, issues
-  // the tile loads; while those run it takes the first softmax part of h
-  // (mask and rescale decisions, rarely taken branches).  Then, branch-free:
-  // the rest of the scores of h+1 next to the exponentials of block 0 of h,
-  // P V of block 0 next to the exponentials of block 1, P V of block 1 next
-  // to the row max of h+1, with the K fragments of h+2 and the V^T fragments
+  // region of half h: the raw scores of h are in registers, as are the K
+  // fragments of half h+1 and the V^T fragments of half h.  The region first
+  // puts a few QK^T MFMAs of h+1 on the pipe (they need nothing from the
+  // softmax) and, in the first half of a tile, issues the tile loads; while
+  // those run it takes the row max and the first softmax part of h (mask and
+  // rescale decisions, rarely taken branches).  Then, branch-free: the rest
+  // of the scores of h+1 next to the exponentials of h, block by block, each
+  // followed by its P V, with the K fragments of h+2 and the V^T fragments
   // of h+1 read from LDS meanwhile.  Past the wave's last half the region
   // computes on stale LDS data whose results are never used.
   struct Half {
-    f32x16 s[2];
+    f32x16 s[NB];
     bf16x8 kf[KSTEPS];
     bf16x8 vf[TBLK][2];
   };
   Half hA, hB;
-  float mx[2];          // row max of the raw scores of the half being retired
-  constexpr int KA = 2; // k-steps of h+1 issued ahead of the softmax branches
+  constexpr int KA = NB == 2 ? 3 : 2;  // k-steps of h+1 issued ahead of the branches
 
   auto issue_tile_loads = [&] __device__ (int TS, int t) __attribute__((always_inline)) {
     load_tile(vbase, v_src, t + 3, VRING + ((TS + 3) & (RING - 1)) * TILE);
@@ -428,24 +439,23 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const int jb2 = jb;
     qk_mfma(nxt.s, cur.kf, 0, KA);
     if (jb == 0) issue_tile_loads(ts, t);
-    float cc[2], mn[2];
+    float cc[NB], mn[NB];
     const int j0 = t * kBC + jb * 32;
-    prepare(cur.s[0], mx[0], 0, j0, cc[0], mn[0]);
-    prepare(cur.s[1], mx[1], 1, j0, cc[1], mn[1]);
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib) prepare(cur.s[ib], row_max(cur.s[ib]), ib, j0, cc[ib], mn[ib]);
     load_kfrags(nxt.kf, slot2, jb2);
     load_vfrags(nxt.vf, slot1, jb1);
     qk_mfma(nxt.s, cur.kf, KA, KSTEPS);
-    bf16x8 p0[2], p1[2];
-    expo(cur.s[0], 0, cc[0], mn[0], p0);
-    pv_mfma(cur.vf, p0, 0);
-    expo(cur.s[1], 1, cc[1], mn[1], p1);
-    pv_mfma(cur.vf, p1, 1);
-    mx[0] = row_max(nxt.s[0]);
-    mx[1] = row_max(nxt.s[1]);
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib) {
+      bf16x8 pk[2];
+      expo(cur.s[ib], ib, cc[ib], mn[ib], pk);
+      pv_mfma(cur.vf, pk, ib);
+    }
   };
 
-  // ---- prologue: K0..K2 and V0..V2 into LDS; raw scores of half 0 and
-  // their max, K fragments of half 1 and V^T fragments of half 0 in registers
+  // ---- prologue: K0..K2 and V0..V2 into LDS; raw scores of half 0, K
+  // fragments of half 1 and V^T fragments of half 0 in registers
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
     load_tile(kbase, k_src, i, KRING + i * TILE);
@@ -458,8 +468,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     qk_mfma(hA.s, hB.kf, 0, KSTEPS);
     load_kfrags(hA.kf, 0, 1);
     load_vfrags(hA.vf, 0, 0);
-    mx[0] = row_max(hA.s[0]);
-    mx[1] = row_max(hA.s[1]);
   }
 
   // one tile t (ring slot TS = t % 4, a constant once inlined): the loads of
@@ -486,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
 
   // ---- epilogue: O = acc / l in bf16, LSE = ln 2 * (m + log2 l)
 #pragma unroll
-  for (int ib = 0; ib < 2; ++ib) {
+  for (int ib = 0; ib < NB; ++ib) {
     const float l_tot = pair_sum(l_run[ib]);
     const int qi = q0b[ib] + col;
     if (wave_tiles == 0 || qi >= L) continue;
@@ -518,12 +526,14 @@ int pick_hwg(int g) {
 template <int D, int HWG>
 int launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int L,
            int n_q, int n_kv, float scale, int causal, hipStream_t stream) {
+  constexpr int NB = kBlocksPerWave;
   constexpr int BR = kCols / HWG;
   const int n_qblk = (L + BR - 1) / BR;
   const long long items_per_qblk = (long long)B * n_kv * ((n_q / n_kv) / HWG);
   const long long grid = items_per_qblk * n_qblk;
   if (items_per_qblk > INT_MAX || grid > INT_MAX) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, HWG>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, HWG, NB>), dim3((unsigned)grid), dim3(kCols / NB * 2), 0,
+                     stream,
                      static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
                      static_cast<const unsigned short*>(v), static_cast<unsigned short*>(out), lse,
                      L, n_q, n_kv, n_qblk, (int)items_per_qblk, scale, causal);
