@@ -492,26 +492,47 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
   }
   wait_vmcnt<0>();   // no tile load may still be writing LDS when the wave ends
 
-  // ---- epilogue: O = acc / l in bf16, LSE = ln 2 * (m + log2 l)
+  // ---- epilogue: O = acc / l in bf16, LSE = ln 2 * (m + log2 l).  Each
+  // block's 32 x d_h output tile goes through LDS (free once every wave is
+  // past the loop and every tile load has landed), so that the global stores
+  // are whole rows: 1 KB per store instruction instead of 8-byte pieces of
+  // 32 different rows.
+  tile_barrier();
+  constexpr int OT = 32 * ROWB;                  // bytes of one block's output tile
+  static_assert(NW * NB * OT <= 2 * RING * TILE, "output staging must fit the rings");
 #pragma unroll
   for (int ib = 0; ib < NB; ++ib) {
     const float l_tot = pair_sum(l_run[ib]);
-    const int qi = q0b[ib] + col;
-    if (wave_tiles == 0 || qi >= L) continue;
     const float inv = 1.0f / l_tot;
-    unsigned short* orow = out + (((size_t)b * n_q + hb[ib]) * L64 + (size_t)qi) * D;
+    LDS_AS unsigned char* ot = smem_l + (wave * NB + ib) * OT;
+    // lane (col, hi) holds row col, columns 32 tb + 8 grp + 4 hi + 0..3
 #pragma unroll
     for (int tb = 0; tb < TBLK; ++tb)
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
-        const int t0 = tb * 32 + grp * 8 + hi * 4;
         bf16x4 o4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[ib][tb][grp * 4 + e] * inv);
-        *reinterpret_cast<u32x2*>(orow + t0) = __builtin_bit_cast(u32x2, o4);
+        const int chunk = tb * 4 + grp;                  // 16-byte chunk of the row
+        *reinterpret_cast<LDS_AS u32x2*>(ot + col * ROWB + ((chunk ^ k_swz<D>(col)) << 4) +
+                                         hi * 8) = __builtin_bit_cast(u32x2, o4);
       }
-    if (hi == 0)
-      lse[((size_t)b * n_q + hb[ib]) * L64 + (size_t)qi] = (m_run[ib] + __log2f(l_tot)) * kLn2;
+    const int q0 = q0b[ib];
+    if (hi == 0 && q0 + col < L && wave_tiles > 0)
+      lse[((size_t)b * n_q + hb[ib]) * L64 + (size_t)(q0 + col)] =
+          (m_run[ib] + __log2f(l_tot)) * kLn2;
+    // read back whole rows: store s covers rows 4 s .. 4 s + 3 (d_h = 128)
+    unsigned short* obase = out + (((size_t)b * n_q + hb[ib]) * L64 + (size_t)q0) * D;
+#pragma unroll
+    for (int st = 0; st < OT / 1024; ++st) {
+      const int byte = st * 1024 + lane * 16;
+      const int row = byte / ROWB;
+      const int chunk = (byte % ROWB) >> 4;
+      const u32x4 v4 =
+          *reinterpret_cast<const LDS_AS u32x4*>(ot + row * ROWB + ((chunk ^ k_swz<D>(row)) << 4));
+      if (q0 + row < L && wave_tiles > 0)
+        *reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8) = v4;
+    }
   }
 }
 
