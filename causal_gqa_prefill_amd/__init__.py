@@ -1,12 +1,16 @@
 """Causal GQA prefill attention for AMD MI355X (gfx950).
 
 attn_prefill(q, k, v, scale=None, causal=True) -> (out, lse) runs the
-hand-written HIP kernels in libattn_prefill.so.  Importing the package loads
+hand-written HIP kernels in libattn_prefill.so; attn_prefill_chunk(q, k, v,
+q_offset) prefills a chunk of queries against a longer key/value sequence, and
+merge_partials(...) combines results over disjoint key sets by their
+log-sum-exp.  Importing the package loads
 nothing; the first use of the attention entry points loads the library and
 raises if it is missing (there is no CPU fallback).
 """
 
-__all__ = ["attn_prefill", "attn_prefill_into", "library", "AttnPrefillError"]
+__all__ = ["attn_prefill", "attn_prefill_into", "attn_prefill_chunk", "attn_prefill_chunk_into",
+           "merge_partials", "library", "AttnPrefillError"]
 
 
 def __getattr__(name):

@@ -41,6 +41,11 @@ def library():
         lib.attn_prefill_fwd.restype = ci
         lib.attn_prefill_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci,
                                          ctypes.c_float, ci, vp]
+        lib.attn_prefill_fwd_chunk.restype = ci
+        lib.attn_prefill_fwd_chunk.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci,
+                                               ctypes.c_float, ci, vp]
+        lib.attn_merge_partials.restype = ci
+        lib.attn_merge_partials.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_longlong, ci, vp]
         lib.attn_prefill_strerror.restype = ctypes.c_char_p
         lib.attn_prefill_strerror.argtypes = [ci]
         lib.attn_prefill_version.restype = ci
@@ -63,7 +68,25 @@ def fwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, L, n_q, n_kv, d_h,
         ctypes.c_void_p(stream_ptr))
 
 
-def _check(q, k, v):
+def fwd_chunk_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, Lq, Lk, q_offset, n_q, n_kv, d_h,
+                  scale, causal, stream_ptr):
+    """Direct call of attn_prefill_fwd_chunk with integer pointers; returns status."""
+    return library().attn_prefill_fwd_chunk(
+        ctypes.c_void_p(q_ptr), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
+        ctypes.c_void_p(out_ptr), ctypes.c_void_p(lse_ptr),
+        int(B), int(Lq), int(Lk), int(q_offset), int(n_q), int(n_kv), int(d_h), float(scale),
+        int(causal), ctypes.c_void_p(stream_ptr))
+
+
+def merge_raw(oa_ptr, la_ptr, ob_ptr, lb_ptr, out_ptr, lo_ptr, rows, d_h, stream_ptr):
+    """Direct call of attn_merge_partials with integer pointers; returns status."""
+    return library().attn_merge_partials(
+        ctypes.c_void_p(oa_ptr), ctypes.c_void_p(la_ptr), ctypes.c_void_p(ob_ptr),
+        ctypes.c_void_p(lb_ptr), ctypes.c_void_p(out_ptr), ctypes.c_void_p(lo_ptr),
+        int(rows), int(d_h), ctypes.c_void_p(stream_ptr))
+
+
+def _check(q, k, v, same_length=True):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
@@ -79,9 +102,10 @@ def _check(q, k, v):
     if not (q.device == k.device == v.device):
         raise ValueError("q, k and v must be on the same device")
     B, n_q, L, d_h = q.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != L or k.shape[3] != d_h:
-        raise ValueError(f"k and v must be [B, n_kv, L, d_h] matching q {tuple(q.shape)}; "
-                         f"got k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if (k.shape != v.shape or k.shape[0] != B or k.shape[3] != d_h
+            or (same_length and k.shape[2] != L)):
+        raise ValueError(f"k and v must be [B, n_kv, {'L' if same_length else 'Lk'}, d_h] "
+                         f"matching q {tuple(q.shape)}; got k {tuple(k.shape)}, v {tuple(v.shape)}")
     return B, n_q, k.shape[1], L, d_h
 
 
@@ -119,3 +143,73 @@ def attn_prefill(q, k, v, scale=None, causal=True, stream=None):
     out = torch.empty_like(q)
     lse = torch.empty((B, n_q, L), dtype=torch.float32, device=q.device)
     return attn_prefill_into(q, k, v, out, lse, scale=scale, causal=causal, stream=stream)
+
+
+def _check_outputs(q, out, lse):
+    import torch
+    B, n_q, L, _ = q.shape
+    if out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, n_q, L) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, n_q, Lq]")
+    if out.device != q.device or lse.device != q.device:
+        raise ValueError("out and lse must be on the inputs' device")
+
+
+def attn_prefill_chunk_into(q, k, v, out, lse, q_offset, scale=None, causal=True, stream=None):
+    """Chunked prefill into caller-provided out and lse: query row i of q sits at
+    key position q_offset + i of k and v (see attn_prefill_fwd_chunk)."""
+    import torch
+    B, n_q, n_kv, Lq, d_h = _check(q, k, v, same_length=False)
+    Lk = k.shape[2]
+    _check_outputs(q, out, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_h)
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        status = fwd_chunk_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, Lq, Lk, q_offset, n_q, n_kv, d_h, scale,
+                               int(bool(causal)), s.cuda_stream)
+    if status != ATTN_PREFILL_OK:
+        raise AttnPrefillError(status, strerror(status))
+    return out, lse
+
+
+def attn_prefill_chunk(q, k, v, q_offset, scale=None, causal=True, stream=None):
+    """Chunked prefill: q bf16 [B, n_q, Lq, d_h] at key positions q_offset ..
+    q_offset + Lq - 1 of k, v bf16 [B, n_kv, Lk, d_h].  Returns (out bf16 like
+    q, lse fp32 [B, n_q, Lq])."""
+    import torch
+    B, n_q, _, Lq, _ = _check(q, k, v, same_length=False)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, n_q, Lq), dtype=torch.float32, device=q.device)
+    return attn_prefill_chunk_into(q, k, v, out, lse, q_offset, scale=scale, causal=causal,
+                                   stream=stream)
+
+
+def merge_partials(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None):
+    """LSE-weighted merge of two partial results over disjoint key sets (see
+    attn_merge_partials).  o_a, o_b: bf16 [..., d_h]; lse_a, lse_b: fp32 with
+    o's shape minus the last axis.  Returns (out, lse_out)."""
+    import torch
+    for name, t in (("o_a", o_a), ("o_b", o_b)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bfloat16 torch.Tensor")
+    for name, t in (("lse_a", lse_a), ("lse_b", lse_b)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous float32 torch.Tensor")
+    if o_a.shape != o_b.shape or lse_a.shape != lse_b.shape or tuple(lse_a.shape) != tuple(o_a.shape[:-1]):
+        raise ValueError("o_a, o_b must match, and lse_a, lse_b must be their shape minus the last axis")
+    if out is None:
+        out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    d_h = o_a.shape[-1]
+    rows = lse_a.numel()
+    with torch.cuda.device(o_a.device):
+        s = stream if stream is not None else torch.cuda.current_stream(o_a.device)
+        status = merge_raw(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(),
+                           out.data_ptr(), lse_out.data_ptr(), rows, d_h, s.cuda_stream)
+    if status != ATTN_PREFILL_OK:
+        raise AttnPrefillError(status, strerror(status))
+    return out, lse_out

@@ -1,4 +1,4 @@
-"""The five attention-layer workloads this library is measured and tested on.
+"""The attention-layer workloads this library is measured and tested on.
 
 Shapes: "flops / prefill-attention", section "Arithmetic intensity", names the
 Llama-2-7B (MHA), Llama-3-8B (GQA-4) and Llama-2-70B (GQA-8) attention
@@ -6,6 +6,10 @@ geometries; "Long-Context Attention Explained" gives the made-up 36-query /
 6-key-value-head, 128-wide shape at 128K tokens.  Inputs are synthetic
 N(0, 1) bf16 tensors drawn from a seed (seed = 1000 + config index); no
 trained weights or activations are involved.
+
+Chunked-prefill workloads ("flops / prefill-attention", section
+"Workarounds": a long prompt prefilled in pieces) put a chunk of Lq queries
+at key position q_offset of a longer K/V; seed = 2000 + index.
 """
 from dataclasses import dataclass
 import math
@@ -57,3 +61,54 @@ CONFIGS = [
 def config(index: int) -> AttnConfig:
     """Config by its 1-based index."""
     return CONFIGS[index - 1]
+
+
+@dataclass(frozen=True)
+class ChunkConfig:
+    index: int
+    name: str
+    B: int
+    Lq: int
+    Lk: int
+    q_offset: int
+    n_q: int
+    n_kv: int
+    d_h: int
+    causal: bool = True
+    sampled_rows: int = 0
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d_h)))
+
+    @property
+    def seed(self) -> int:
+        return 2000 + self.index
+
+    def visible_pairs(self) -> int:
+        """(query, key) pairs per head that attention actually forms."""
+        if not self.causal:
+            return self.Lq * self.Lk
+        first = self.q_offset + 1
+        last = self.q_offset + self.Lq
+        return (first + last) * self.Lq // 2
+
+    def flops(self) -> int:
+        """2 * d_h flops per visible pair for Q K^T and as many for P V."""
+        return 4 * self.B * self.n_q * self.d_h * self.visible_pairs()
+
+    def describe(self) -> str:
+        return (f"{self.name}: B={self.B} Lq={self.Lq} Lk={self.Lk} q_offset={self.q_offset} "
+                f"n_q={self.n_q} n_kv={self.n_kv} d_h={self.d_h} causal={int(self.causal)}")
+
+
+CHUNK_CONFIGS = [
+    ChunkConfig(1, "Llama-3-8B-shaped GQA-4, last 4K chunk of a 32K prompt",
+                1, 4096, 32768, 28672, 32, 8, 128, sampled_rows=2048),
+    ChunkConfig(2, "Llama-2-70B-shaped GQA-8, 2K chunk at 8K of a 16K cache",
+                1, 2048, 16384, 8192, 64, 8, 128, sampled_rows=2048),
+]
+
+
+def chunk_config(index: int) -> ChunkConfig:
+    return CHUNK_CONFIGS[index - 1]

@@ -147,13 +147,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 // One wave's share of a K or V tile load, global -> LDS: `loads` loads of
 // 1 KB, lane i of load s bringing the 16 bytes at source offset src[s]
 // (relative to row j0 of rows of `row_bytes`) to LDS byte dst + 1 KB s + 16 i.
-// A tile at or past row L reads as zeros and touches no memory.
+// A tile at or past row L reads as zeros and touches no memory.  The range
+// covers at most one tile, so it fits the 32-bit record count at any L.
 __device__ __forceinline__ void dma_tile(const unsigned short* base, const int* src, int loads,
                                          int row_bytes, int j0, int L, unsigned char* dst_shared) {
   LDS_AS unsigned char* dst = (LDS_AS unsigned char*)dst_shared;
   const __amdgpu_buffer_rsrc_t rsrc =
       make_rsrc((const unsigned char*)base + (size_t)j0 * row_bytes,
-                (unsigned)max(L - j0, 0) * row_bytes);
+                (unsigned)min(max(L - j0, 0), kBC) * row_bytes);
 #pragma unroll
   for (int s = 0; s < loads; ++s)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + s * 1024), 16, src[s], 0,
@@ -164,8 +165,8 @@ template <int D, int HWG, int NB>
 __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ out,
-    float* __restrict__ lse, int L, int n_q, int n_kv, int n_qblk, int items_per_qblk,
-    float scale, int causal) {
+    float* __restrict__ lse, int Lq, int Lk, int q_off, int n_q, int n_kv, int n_qblk,
+    int items_per_qblk, float scale, int causal) {
   constexpr int NW = kCols / (32 * NB);        // waves per workgroup
   constexpr int BR = kCols / HWG;              // query rows per workgroup
   constexpr int KSTEPS = D / 16;               // k-steps of Q K^T
@@ -208,29 +209,31 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     q0b[ib] = qb * BR + c0 % BR;
   }
 
-  const size_t L64 = (size_t)L;
-  const unsigned short* kbase = k + ((size_t)b * n_kv + kvh) * L64 * D;
-  const unsigned short* vbase = v + ((size_t)b * n_kv + kvh) * L64 * D;
+  // query row i sits at key position q_off + i; K and V hold Lk rows
+  const size_t Lq64 = (size_t)Lq;
+  const unsigned short* kbase = k + ((size_t)b * n_kv + kvh) * (size_t)Lk * D;
+  const unsigned short* vbase = v + ((size_t)b * n_kv + kvh) * (size_t)Lk * D;
 
   // ---- tiles the workgroup streams, and tiles this wave computes
-  const int wg_end = min(qb * BR + BR, L);
-  const int n_tiles = causal ? (wg_end + kBC - 1) / kBC : (L + kBC - 1) / kBC;
+  const int wg_end = min(qb * BR + BR, Lq);
+  const int n_tiles = causal ? (wg_end + q_off + kBC - 1) / kBC : (Lk + kBC - 1) / kBC;
   int last_row = -1;
 #pragma unroll
   for (int ib = 0; ib < NB; ++ib)
-    if (q0b[ib] < L) last_row = max(last_row, min(q0b[ib] + 31, L - 1));
-  const int wave_tiles = last_row < 0 ? 0 : (causal ? last_row / kBC + 1 : n_tiles);
+    if (q0b[ib] < Lq) last_row = max(last_row, min(q0b[ib] + 31, Lq - 1));
+  const int wave_tiles =
+      last_row < 0 ? 0 : (causal ? (last_row + q_off) / kBC + 1 : n_tiles);
 
   // ---- Q fragments (B operand of S^T = K Q^T): Q[row][16 kk + 8 hi + 0..7]
   bf16x8 qf[NB][KSTEPS];
 #pragma unroll
   for (int ib = 0; ib < NB; ++ib) {
     const int qi = q0b[ib] + col;
-    const unsigned short* qrow = q + (((size_t)b * n_q + hb[ib]) * L64 + (size_t)qi) * D;
+    const unsigned short* qrow = q + (((size_t)b * n_q + hb[ib]) * Lq64 + (size_t)qi) * D;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (qi < L) raw = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hi * 8);
+      if (qi < Lq) raw = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hi * 8);
       qf[ib][kk] = __builtin_bit_cast(bf16x8, raw);
     }
   }
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
   }
   auto load_tile = [&] __device__ (const unsigned short* base, const int (&src)[LOADS], int tile,
                        int lds_off) __attribute__((always_inline)) {
-    dma_tile(base, src, LOADS, ROWB, tile * kBC, L, smem + lds_off + wave * LOADS * 1024);
+    dma_tile(base, src, LOADS, ROWB, tile * kBC, Lk, smem + lds_off + wave * LOADS * 1024);
   };
 
   // ---- per-lane LDS read offsets
@@ -352,7 +355,8 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
   };
 
   // softmax, first part, for the scores of keys j0 .. j0+31 (may branch):
-  // where the half straddles the diagonal or the end of the sequence, or the
+  // where the half straddles the diagonal (query q0 + i sees keys up to
+  // q_off + q0 + i) or the end of the keys, or the
   // scale is not positive, mask and pre-scale the scores and retake the row
   // max; then move the reference max (rescaling l and acc) only when the
   // tile max exceeds it by more than 2^8.  Returns the multiplier and -m.
@@ -360,13 +364,13 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
                                  float& mneg_out) __attribute__((always_inline)) {
     const int q0 = q0b[ib];
     const int qi = q0 + col;
-    const bool need_mask = (causal && j0 + 31 > q0) || (j0 + 32 > L);
+    const bool need_mask = (causal && j0 + 31 > q0 + q_off) || (j0 + 32 > Lk);
     float c = c2;
     if (need_mask || !fast_scale) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = j0 + (r >> 2) * 8 + hi * 4 + (r & 3);
-        const bool dead = (causal && j > qi) || j >= L;
+        const bool dead = (causal && j > qi + q_off) || j >= Lk;
         s[r] = dead ? -INFINITY : s[r] * c2;
       }
       c = 1.0f;
@@ -518,11 +522,11 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
                                          hi * 8) = __builtin_bit_cast(u32x2, o4);
       }
     const int q0 = q0b[ib];
-    if (hi == 0 && q0 + col < L && wave_tiles > 0)
-      lse[((size_t)b * n_q + hb[ib]) * L64 + (size_t)(q0 + col)] =
+    if (hi == 0 && q0 + col < Lq && wave_tiles > 0)
+      lse[((size_t)b * n_q + hb[ib]) * Lq64 + (size_t)(q0 + col)] =
           (m_run[ib] + __log2f(l_tot)) * kLn2;
     // read back whole rows: store s covers rows 4 s .. 4 s + 3 (d_h = 128)
-    unsigned short* obase = out + (((size_t)b * n_q + hb[ib]) * L64 + (size_t)q0) * D;
+    unsigned short* obase = out + (((size_t)b * n_q + hb[ib]) * Lq64 + (size_t)q0) * D;
 #pragma unroll
     for (int st = 0; st < OT / 1024; ++st) {
       const int byte = st * 1024 + lane * 16;
@@ -530,7 +534,7 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
       const int chunk = (byte % ROWB) >> 4;
       const u32x4 v4 =
           *reinterpret_cast<const LDS_AS u32x4*>(ot + row * ROWB + ((chunk ^ k_swz<D>(row)) << 4));
-      if (q0 + row < L && wave_tiles > 0)
+      if (q0 + row < Lq && wave_tiles > 0)
         *reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8) = v4;
     }
   }
@@ -544,31 +548,37 @@ int pick_hwg(int g) {
   return 1;
 }
 
+// Sizes of one call; Lq = Lk and q_off = 0 for a whole-sequence prefill.
+struct Shape {
+  int B, Lq, Lk, q_off, n_q, n_kv, d_h;
+};
+
 template <int D, int HWG>
-int launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int L,
-           int n_q, int n_kv, float scale, int causal, hipStream_t stream) {
+int launch(const void* q, const void* k, const void* v, void* out, float* lse, const Shape& sh,
+           float scale, int causal, hipStream_t stream) {
   constexpr int NB = kBlocksPerWave;
   constexpr int BR = kCols / HWG;
-  const int n_qblk = (L + BR - 1) / BR;
-  const long long items_per_qblk = (long long)B * n_kv * ((n_q / n_kv) / HWG);
+  const int n_qblk = (sh.Lq + BR - 1) / BR;
+  const long long items_per_qblk = (long long)sh.B * sh.n_kv * ((sh.n_q / sh.n_kv) / HWG);
   const long long grid = items_per_qblk * n_qblk;
   if (items_per_qblk > INT_MAX || grid > INT_MAX) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
   hipLaunchKernelGGL((attn_fwd_kernel<D, HWG, NB>), dim3((unsigned)grid), dim3(kCols / NB * 2), 0,
                      stream,
                      static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
                      static_cast<const unsigned short*>(v), static_cast<unsigned short*>(out), lse,
-                     L, n_q, n_kv, n_qblk, (int)items_per_qblk, scale, causal);
+                     sh.Lq, sh.Lk, sh.q_off, sh.n_q, sh.n_kv, n_qblk, (int)items_per_qblk, scale,
+                     causal);
   return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
 }
 
 template <int D>
-int launch_d(const void* q, const void* k, const void* v, void* out, float* lse, int B, int L,
-             int n_q, int n_kv, float scale, int causal, hipStream_t stream) {
-  switch (pick_hwg(n_q / n_kv)) {
-    case 8: return launch<D, 8>(q, k, v, out, lse, B, L, n_q, n_kv, scale, causal, stream);
-    case 4: return launch<D, 4>(q, k, v, out, lse, B, L, n_q, n_kv, scale, causal, stream);
-    case 2: return launch<D, 2>(q, k, v, out, lse, B, L, n_q, n_kv, scale, causal, stream);
-    default: return launch<D, 1>(q, k, v, out, lse, B, L, n_q, n_kv, scale, causal, stream);
+int launch_d(const void* q, const void* k, const void* v, void* out, float* lse, const Shape& sh,
+             float scale, int causal, hipStream_t stream) {
+  switch (pick_hwg(sh.n_q / sh.n_kv)) {
+    case 8: return launch<D, 8>(q, k, v, out, lse, sh, scale, causal, stream);
+    case 4: return launch<D, 4>(q, k, v, out, lse, sh, scale, causal, stream);
+    case 2: return launch<D, 2>(q, k, v, out, lse, sh, scale, causal, stream);
+    default: return launch<D, 1>(q, k, v, out, lse, sh, scale, causal, stream);
   }
 }
 
@@ -577,17 +587,18 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return x < y + bn && y < x + an;
 }
 
-}  // namespace
-
-extern "C" int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out,
-                                float* lse, int B, int L, int n_q, int n_kv, int d_h,
-                                float scale, int causal, hipStream_t stream) {
+// Argument checks shared by the entry points, then the launch.
+int check_and_launch(const void* q, const void* k, const void* v, void* out, float* lse,
+                     const Shape& sh, float scale, int causal, hipStream_t stream) {
   if (!q || !k || !v || !out || !lse) return ATTN_PREFILL_ERR_NULL_PTR;
-  if (B < 1 || L < 1 || n_q < 1 || n_kv < 1) return ATTN_PREFILL_ERR_BAD_SHAPE;
-  if (n_q % n_kv != 0) return ATTN_PREFILL_ERR_BAD_GQA;
-  if (d_h != 64 && d_h != 128) return ATTN_PREFILL_ERR_BAD_HEADDIM;
+  if (sh.B < 1 || sh.Lq < 1 || sh.Lk < 1 || sh.n_q < 1 || sh.n_kv < 1)
+    return ATTN_PREFILL_ERR_BAD_SHAPE;
+  if (sh.n_q % sh.n_kv != 0) return ATTN_PREFILL_ERR_BAD_GQA;
+  if (sh.d_h != 64 && sh.d_h != 128) return ATTN_PREFILL_ERR_BAD_HEADDIM;
   if (!std::isfinite(scale)) return ATTN_PREFILL_ERR_BAD_SCALE;
   if (causal != 0 && causal != 1) return ATTN_PREFILL_ERR_BAD_CAUSAL;
+  if (sh.q_off < 0 || (causal && (long long)sh.q_off + sh.Lq > sh.Lk))
+    return ATTN_PREFILL_ERR_BAD_OFFSET;
   const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out);
   if ((align & 15) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3) != 0)
@@ -595,12 +606,12 @@ extern "C" int attn_prefill_fwd(const void* q, const void* k, const void* v, voi
 
   // element counts, checked for 64-bit overflow (bytes must fit in 2^62)
   size_t lse_elems, q_elems, kv_rows, kv_elems;
-  if (__builtin_mul_overflow((size_t)B, (size_t)n_q, &lse_elems) ||
-      __builtin_mul_overflow(lse_elems, (size_t)L, &lse_elems) ||
-      __builtin_mul_overflow(lse_elems, (size_t)d_h, &q_elems) ||
-      __builtin_mul_overflow((size_t)B, (size_t)n_kv, &kv_rows) ||
-      __builtin_mul_overflow(kv_rows, (size_t)L, &kv_rows) ||
-      __builtin_mul_overflow(kv_rows, (size_t)d_h, &kv_elems) ||
+  if (__builtin_mul_overflow((size_t)sh.B, (size_t)sh.n_q, &lse_elems) ||
+      __builtin_mul_overflow(lse_elems, (size_t)sh.Lq, &lse_elems) ||
+      __builtin_mul_overflow(lse_elems, (size_t)sh.d_h, &q_elems) ||
+      __builtin_mul_overflow((size_t)sh.B, (size_t)sh.n_kv, &kv_rows) ||
+      __builtin_mul_overflow(kv_rows, (size_t)sh.Lk, &kv_rows) ||
+      __builtin_mul_overflow(kv_rows, (size_t)sh.d_h, &kv_elems) ||
       q_elems > ((size_t)1 << 61) || kv_elems > ((size_t)1 << 61))
     return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
   const size_t q_bytes = q_elems * 2, kv_bytes = kv_elems * 2, lse_bytes = lse_elems * 4;
@@ -610,15 +621,105 @@ extern "C" int attn_prefill_fwd(const void* q, const void* k, const void* v, voi
       overlaps(lse, lse_bytes, v, kv_bytes))
     return ATTN_PREFILL_ERR_ALIASING;
 
-  if (d_h == 128) return launch_d<128>(q, k, v, out, lse, B, L, n_q, n_kv, scale, causal, stream);
-  return launch_d<64>(q, k, v, out, lse, B, L, n_q, n_kv, scale, causal, stream);
+  if (sh.d_h == 128) return launch_d<128>(q, k, v, out, lse, sh, scale, causal, stream);
+  return launch_d<64>(q, k, v, out, lse, sh, scale, causal, stream);
+}
+
+// ---- merge of two partial results over disjoint key sets ("Long-Context
+// Attention Explained", section "Online softmax": the running max and sum of
+// two parts combine by rescaling each to the larger max).  One thread per 8
+// elements of a row; d_h / 8 threads per row.
+__global__ __launch_bounds__(256) void merge_kernel(
+    const unsigned short* __restrict__ oa, const float* __restrict__ la,
+    const unsigned short* __restrict__ ob, const float* __restrict__ lb,
+    unsigned short* __restrict__ out, float* __restrict__ lo, long long rows, int d_h) {
+  const int per_row = d_h / 8;
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long row = gid / per_row;
+  if (row >= rows) return;
+  const int c8 = (int)(gid % per_row) * 8;
+  const float a = la[row], bb = lb[row];
+  const float m = fmaxf(a, bb);
+  // a side with lse = -inf (no visible key) gets weight 0; both: O = 0, lse -inf
+  const float wa = a == -INFINITY ? 0.0f : __expf(a - m);
+  const float wb = bb == -INFINITY ? 0.0f : __expf(bb - m);
+  const float sum = wa + wb;
+  const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+  // a weight-0 side adds nothing, even if its o holds NaN or garbage: its
+  // bits are masked to zero (integer arithmetic, which no floating-point
+  // assumption of the compiler can fold away)
+  const unsigned keep_a = wa > 0.0f ? 0xffffffffu : 0u;
+  const unsigned keep_b = wb > 0.0f ? 0xffffffffu : 0u;
+  const u32x4 va = *reinterpret_cast<const u32x4*>(oa + row * d_h + c8);
+  const u32x4 vb = *reinterpret_cast<const u32x4*>(ob + row * d_h + c8);
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16x2 xa = __builtin_bit_cast(bf16x2, va[e] & keep_a);
+    const bf16x2 xb = __builtin_bit_cast(bf16x2, vb[e] & keep_b);
+    bf16x2 y;
+    y[0] = (__bf16)(((float)xa[0] * wa + (float)xb[0] * wb) * inv);
+    y[1] = (__bf16)(((float)xa[1] * wa + (float)xb[1] * wb) * inv);
+    r[e] = __builtin_bit_cast(unsigned, y);
+  }
+  *reinterpret_cast<u32x4*>(out + row * d_h + c8) = r;
+  if (c8 == 0) lo[row] = sum > 0.0f ? m + __logf(sum) : -INFINITY;
+}
+
+}  // namespace
+
+extern "C" int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out,
+                                float* lse, int B, int L, int n_q, int n_kv, int d_h,
+                                float scale, int causal, hipStream_t stream) {
+  return check_and_launch(q, k, v, out, lse, Shape{B, L, L, 0, n_q, n_kv, d_h}, scale, causal,
+                          stream);
+}
+
+extern "C" int attn_prefill_fwd_chunk(const void* q, const void* k, const void* v, void* out,
+                                      float* lse, int B, int Lq, int Lk, int q_offset, int n_q,
+                                      int n_kv, int d_h, float scale, int causal,
+                                      hipStream_t stream) {
+  return check_and_launch(q, k, v, out, lse, Shape{B, Lq, Lk, q_offset, n_q, n_kv, d_h}, scale,
+                          causal, stream);
+}
+
+extern "C" int attn_merge_partials(const void* o_a, const float* lse_a, const void* o_b,
+                                   const float* lse_b, void* out, float* lse_out, long long rows,
+                                   int d_h, hipStream_t stream) {
+  if (!o_a || !lse_a || !o_b || !lse_b || !out || !lse_out) return ATTN_PREFILL_ERR_NULL_PTR;
+  if (rows < 1) return ATTN_PREFILL_ERR_BAD_SHAPE;
+  if (d_h != 64 && d_h != 128) return ATTN_PREFILL_ERR_BAD_HEADDIM;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(o_a) | reinterpret_cast<uintptr_t>(o_b) |
+                          reinterpret_cast<uintptr_t>(out);
+  const uintptr_t align4 = reinterpret_cast<uintptr_t>(lse_a) |
+                           reinterpret_cast<uintptr_t>(lse_b) |
+                           reinterpret_cast<uintptr_t>(lse_out);
+  if ((align & 15) != 0 || (align4 & 3) != 0) return ATTN_PREFILL_ERR_MISALIGNED;
+  size_t elems;
+  if (__builtin_mul_overflow((size_t)rows, (size_t)d_h, &elems) || elems > ((size_t)1 << 61))
+    return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  const size_t ob = elems * 2, lb = (size_t)rows * 4;
+  // out may not overlap anything; inputs may overlap each other (read only)
+  if (overlaps(out, ob, o_a, ob) || overlaps(out, ob, o_b, ob) || overlaps(out, ob, lse_a, lb) ||
+      overlaps(out, ob, lse_b, lb) || overlaps(out, ob, lse_out, lb) ||
+      overlaps(lse_out, lb, o_a, ob) || overlaps(lse_out, lb, o_b, ob) ||
+      overlaps(lse_out, lb, lse_a, lb) || overlaps(lse_out, lb, lse_b, lb))
+    return ATTN_PREFILL_ERR_ALIASING;
+  const long long threads = (long long)rows * (d_h / 8);
+  const long long blocks = (threads + 255) / 256;
+  if (blocks > INT_MAX) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const unsigned short*>(o_a), lse_a,
+                     static_cast<const unsigned short*>(o_b), lse_b,
+                     static_cast<unsigned short*>(out), lse_out, rows, d_h);
+  return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
 }
 
 extern "C" const char* attn_prefill_strerror(int status) {
   switch (status) {
     case ATTN_PREFILL_OK: return "success";
     case ATTN_PREFILL_ERR_NULL_PTR: return "a buffer pointer is NULL";
-    case ATTN_PREFILL_ERR_BAD_SHAPE: return "B, L, n_q and n_kv must be >= 1";
+    case ATTN_PREFILL_ERR_BAD_SHAPE: return "B, L (Lq, Lk, rows), n_q and n_kv must be >= 1";
     case ATTN_PREFILL_ERR_BAD_GQA: return "n_q must be a multiple of n_kv";
     case ATTN_PREFILL_ERR_BAD_HEADDIM: return "d_h must be 64 or 128";
     case ATTN_PREFILL_ERR_BAD_SCALE: return "scale must be finite";
@@ -628,8 +729,10 @@ extern "C" const char* attn_prefill_strerror(int status) {
     case ATTN_PREFILL_ERR_SIZE_OVERFLOW: return "sizes overflow the supported range";
     case ATTN_PREFILL_ERR_ALIASING: return "out or lse overlaps another buffer";
     case ATTN_PREFILL_ERR_LAUNCH: return "HIP kernel launch failed";
+    case ATTN_PREFILL_ERR_BAD_OFFSET:
+      return "q_offset must be >= 0, and q_offset + Lq <= Lk when causal";
     default: return "unknown status";
   }
 }
 
-extern "C" int attn_prefill_version(void) { return 100; }
+extern "C" int attn_prefill_version(void) { return 200; }

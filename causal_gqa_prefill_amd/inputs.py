@@ -45,6 +45,41 @@ def make_config_qkv(cfg):
     return make_qkv(cfg.B, cfg.L, cfg.n_q, cfg.n_kv, cfg.d_h, cfg.seed)
 
 
+def make_chunk_qkv(B, Lq, Lk, n_q, n_kv, d_h, seed):
+    """A chunk's Q [B,n_q,Lq,d_h] and the K, V [B,n_kv,Lk,d_h] it attends to,
+    as bf16 bits from N(0, 1), drawn in the order Q, K, V from one stream."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for heads, length in ((n_q, Lq), (n_kv, Lk), (n_kv, Lk)):
+        x = rng.standard_normal((B, heads, length, d_h), dtype=np.float32)
+        out.append(bf16_bits(x))
+        del x
+    return tuple(out)
+
+
+def make_partials(rows, d_h, seed, empty_every=0):
+    """Two partial results to merge: o_a, o_b bf16 bits [rows, d_h] from
+    N(0, 1) and lse_a, lse_b float32 [rows] from 8 * N(0, 1) (so the two
+    weights range from equal to many orders apart).  With empty_every = n > 0,
+    every n-th row has lse_a = -inf, every n-th row offset by n // 2 has
+    lse_b = -inf, every n-th row offset by n // 3 has both, and an empty side's
+    o holds NaN bits (its content must not matter)."""
+    rng = np.random.default_rng(seed)
+    o_a = bf16_bits(rng.standard_normal((rows, d_h), dtype=np.float32))
+    o_b = bf16_bits(rng.standard_normal((rows, d_h), dtype=np.float32))
+    lse_a = (8.0 * rng.standard_normal(rows)).astype(np.float32)
+    lse_b = (8.0 * rng.standard_normal(rows)).astype(np.float32)
+    if empty_every > 0:
+        r = np.arange(rows)
+        ea = (r % empty_every == 0) | (r % empty_every == empty_every // 3)
+        eb = (r % empty_every == empty_every // 2) | (r % empty_every == empty_every // 3)
+        lse_a[ea] = -np.inf
+        lse_b[eb] = -np.inf
+        o_a[ea] = 0x7FC0
+        o_b[eb] = 0x7FC0
+    return o_a, lse_a, o_b, lse_b
+
+
 def sample_rows(B, n_q, L, n, seed, block_rows=128):
     """n distinct flat row ids (b * n_q + h) * L + i.
 

@@ -59,3 +59,27 @@ def l_ridge(ridge_flop_per_byte, g):
 def attainable(intensity, p_max, beta):
     """Roofline: min(P_max, beta * I)."""
     return min(p_max, beta * intensity)
+
+
+def chunk_flops(B, Lq, Lk, q_offset, n_q, d_h, causal=True):
+    """Flops of a chunk ("flops / prefill-attention", section "Workarounds"):
+    4 * d_h per (query, key) pair formed; causally query i of the chunk sees
+    q_offset + i + 1 keys, otherwise all Lk."""
+    if causal:
+        pairs = (2 * q_offset + Lq + 1) * Lq // 2
+    else:
+        pairs = Lq * Lk
+    return 4 * d_h * pairs * B * n_q
+
+
+def chunk_bytes(B, Lq, Lk, n_q, n_kv, d_h, elem=2):
+    """Compulsory HBM bytes of a chunk: read Q and the K, V rows, write O and
+    the fp32 LSE (a causal chunk at q_offset reads only q_offset + Lq rows
+    of K and V; this counts all Lk, the non-causal case)."""
+    return 2 * B * n_q * Lq * d_h * elem + kv_bytes(B, Lk, n_kv, d_h, elem) + 4 * B * n_q * Lq
+
+
+def merge_bytes(rows, d_h, elem=2):
+    """Bytes of one merge: read two [rows, d_h] partials and two fp32 LSE
+    rows, write one of each."""
+    return 3 * rows * d_h * elem + 3 * rows * 4

@@ -69,7 +69,9 @@ enum attn_prefill_status {
                                            lse not 4-byte aligned              */
     ATTN_PREFILL_ERR_SIZE_OVERFLOW = 8, /* a size or the grid overflows        */
     ATTN_PREFILL_ERR_ALIASING = 9,      /* out or lse overlaps another buffer  */
-    ATTN_PREFILL_ERR_LAUNCH = 10        /* the HIP launch failed               */
+    ATTN_PREFILL_ERR_LAUNCH = 10,       /* the HIP launch failed               */
+    ATTN_PREFILL_ERR_BAD_OFFSET = 11    /* q_offset < 0, or (causal)
+                                           q_offset + Lq > Lk                  */
 };
 
 /*
@@ -87,6 +89,49 @@ enum attn_prefill_status {
 int attn_prefill_fwd(const void *q, const void *k, const void *v, void *out,
                      float *lse, int B, int L, int n_q, int n_kv, int d_h,
                      float scale, int causal, hipStream_t stream);
+
+/*
+ * Chunked prefill: a chunk of Lq queries against Lk keys, query row i sitting
+ * at key position q_offset + i.  This is how a long prompt is prefilled in
+ * pieces against the keys and values already computed for the earlier pieces
+ * ("flops / prefill-attention", section "Workarounds", chunked prefill), and
+ * with Lq = Lk, q_offset = 0 it is attn_prefill_fwd.
+ *   q, out : bf16 [B, n_q, Lq, d_h];  k, v : bf16 [B, n_kv, Lk, d_h];
+ *   lse    : fp32 [B, n_q, Lq]
+ *   causal : 1 = key j visible to query row i iff j <= q_offset + i
+ *            (requires q_offset + Lq <= Lk, so every query sees its own
+ *            position); 0 = all Lk keys visible (q_offset is then unused)
+ *   q_offset >= 0; other arguments, numerics, ownership and errors as for
+ *   attn_prefill_fwd, ATTN_PREFILL_ERR_BAD_OFFSET for a bad q_offset.
+ */
+int attn_prefill_fwd_chunk(const void *q, const void *k, const void *v, void *out,
+                           float *lse, int B, int Lq, int Lk, int q_offset, int n_q,
+                           int n_kv, int d_h, float scale, int causal,
+                           hipStream_t stream);
+
+/*
+ * Merge of two partial attention results over disjoint key sets into the
+ * result over their union: with m = max(lse_a, lse_b),
+ * w_x = exp(lse_x - m),
+ *     out     = (w_a o_a + w_b o_b) / (w_a + w_b),
+ *     lse_out = m + ln(w_a + w_b).
+ * This is the online-softmax step ("Long-Context Attention Explained",
+ * section "Online softmax": two running maxima and sums combine by rescaling
+ * to the larger max) applied to finished rows, so a query block can attend
+ * to keys held in separate buffers (say a cached prefix and the chunk's own
+ * keys) or split over launches.  A side whose weight is 0 (lse = -inf: no
+ * visible key) contributes nothing, whatever its o holds; if both lse are
+ * -inf the row is 0 with lse -inf.
+ *   o_a, o_b, out      : device pointers, bf16 [rows, d_h] (any row-major
+ *                        tensor whose last axis is d_h, e.g. [B, n_q, L, d_h])
+ *   lse_a, lse_b, lse_out : device pointers, fp32 [rows]
+ *   rows >= 1, d_h in {64, 128}; out and lse_out may not overlap any other
+ *   buffer (the inputs may overlap each other).  Arithmetic in fp32, out
+ *   rounded to bf16 (nearest even).  Errors as for attn_prefill_fwd.
+ */
+int attn_merge_partials(const void *o_a, const float *lse_a, const void *o_b,
+                        const float *lse_b, void *out, float *lse_out, long long rows,
+                        int d_h, hipStream_t stream);
 
 /* Static text for a status code (never NULL). */
 const char *attn_prefill_strerror(int status);

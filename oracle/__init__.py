@@ -34,6 +34,15 @@ def load_library(path):
         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
         ctypes.POINTER(ctypes.c_uint64), ctypes.c_int,
     ]
+    lib.oracle_attn_rows_chunk.restype = ctypes.c_int
+    lib.oracle_attn_rows_chunk.argtypes = [
+        u16p, u16p, u16p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+        ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+        ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+        ctypes.POINTER(ctypes.c_uint64), ctypes.c_int,
+    ]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_version.restype = ctypes.c_int
     return lib
@@ -98,3 +107,76 @@ def attention_rows(q, k, v, scale, causal=True, rows=None, threads=0, lib=None):
     if rc != OK:
         raise ValueError(f"oracle_attn_rows failed with code {rc}")
     return out, lse, int(flops.value)
+
+
+def attention_rows_chunk(q, k, v, scale, causal=True, q_offset=0, rows=None, threads=0,
+                         lib=None):
+    """Oracle attention of a chunk: Lq queries, query row i at key position
+    q_offset + i, against Lk keys ("flops / prefill-attention", section
+    "Workarounds", chunked prefill).
+
+    q: uint16 [B, n_q, Lq, d_h]; k, v: uint16 [B, n_kv, Lk, d_h] (bf16 bits).
+    causal: key j visible to row i iff j <= q_offset + i (needs
+    q_offset + Lq <= Lk); otherwise all Lk keys.
+    rows: None for every row, else flat row ids (b * n_q + h) * Lq + i.
+    Returns (out [n_rows, d_h] float64, lse [n_rows] float64, flops int).
+    """
+    if q.ndim != 4 or k.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B, heads, L, d_h]")
+    B, n_q, Lq, d_h = q.shape
+    n_kv, Lk = k.shape[1], k.shape[2]
+    q = _bits(q, (B, n_q, Lq, d_h), "q")
+    k = _bits(k, (B, n_kv, Lk, d_h), "k")
+    v = _bits(v, (B, n_kv, Lk, d_h), "v")
+    if rows is None:
+        n_rows = B * n_q * Lq
+        rows_p = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = int(rows.size)
+        rows_p = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    out = np.empty((n_rows, d_h), dtype=np.float64)
+    lse = np.empty((n_rows,), dtype=np.float64)
+    flops = ctypes.c_uint64(0)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = (lib or _load()).oracle_attn_rows_chunk(
+        q.ctypes.data_as(u16p), k.ctypes.data_as(u16p), v.ctypes.data_as(u16p),
+        B, Lq, Lk, int(q_offset), n_q, n_kv, d_h, float(np.float32(scale)), int(causal),
+        rows_p, n_rows, out.ctypes.data_as(dp), lse.ctypes.data_as(dp),
+        ctypes.byref(flops), int(threads))
+    if rc != OK:
+        raise ValueError(f"oracle_attn_rows_chunk failed with code {rc}")
+    return out, lse, int(flops.value)
+
+
+def merge_partials(o_a, lse_a, o_b, lse_b):
+    """Merge of two partial attention results over disjoint key sets, in
+    float64 ("Long-Context Attention Explained", section "Online softmax":
+    two running maxima and sums combine by rescaling to the larger max).
+
+    o_a, o_b: [rows, d_h] partial outputs (each a softmax-weighted average
+    over its own keys); lse_a, lse_b: [rows] their natural-log LSEs, -inf
+    for a side with no visible key.  Returns (out [rows, d_h], lse [rows]):
+    out = (w_a o_a + w_b o_b) / (w_a + w_b), lse = m + ln(w_a + w_b), with
+    m = max(lse_a, lse_b) and w_x = exp(lse_x - m); a side of weight 0 adds
+    nothing whatever its o holds (a side with no key may be left unwritten);
+    a row with both sides -inf gives out 0 and lse -inf.
+    """
+    o_a = np.asarray(o_a, dtype=np.float64)
+    o_b = np.asarray(o_b, dtype=np.float64)
+    lse_a = np.asarray(lse_a, dtype=np.float64)
+    lse_b = np.asarray(lse_b, dtype=np.float64)
+    m = np.maximum(lse_a, lse_b)
+    both_empty = np.isneginf(m)
+    m_safe = np.where(both_empty, 0.0, m)
+    w_a = np.where(np.isneginf(lse_a), 0.0, np.exp(lse_a - m_safe))
+    w_b = np.where(np.isneginf(lse_b), 0.0, np.exp(lse_b - m_safe))
+    total = w_a + w_b
+    safe_total = np.where(both_empty, 1.0, total)
+    # a side of weight 0 contributes nothing, whatever its output holds
+    part_a = np.where(w_a[:, None] > 0, w_a[:, None] * o_a, 0.0)
+    part_b = np.where(w_b[:, None] > 0, w_b[:, None] * o_b, 0.0)
+    out = (part_a + part_b) / safe_total[:, None]
+    lse = np.where(both_empty, -np.inf, m_safe + np.log(safe_total))
+    return out, lse

@@ -28,9 +28,15 @@
  * the caller's fp32 value, widened exactly; inputs are bf16 bit patterns,
  * widened exactly to fp64; everything after that is fp64.
  *
- * Layouts: q [B, n_q, L, d_h], k and v [B, n_kv, L, d_h], all bf16 bit
+ * Chunked prefill ("flops / prefill-attention", section "Workarounds": a long
+ * prompt split into pieces): a chunk of Lq queries against Lk keys, query
+ * row i sitting at key position q_off + i, so that causally it sees keys
+ * j <= q_off + i.  With Lq = Lk = L and q_off = 0 this is the whole-sequence
+ * case above.
+ *
+ * Layouts: q [B, n_q, Lq, d_h], k and v [B, n_kv, Lk, d_h], all bf16 bit
  * patterns (uint16), row-major, d_h fastest.  A "row" is the flat index
- * (b * n_q + h) * L + i of one query.
+ * (b * n_q + h) * Lq + i of one query.
  *
  * Parity pins: every function here is pinned by CPU tests against brute force
  * in 50-digit arithmetic, closed forms and a library routine; nothing in it is
@@ -48,7 +54,7 @@
 #define ORACLE_BAD_ARG 1
 #define ORACLE_NO_MEMORY 2
 
-int oracle_version(void) { return 1; }
+int oracle_version(void) { return 2; }
 
 /* A bf16 bit pattern is the upper half of an fp32 bit pattern, so widening is
  * exact: shift into place, reinterpret as float, convert to double. */
@@ -60,23 +66,24 @@ static double widen_bf16(uint16_t bits)
     return (double)f;
 }
 
-/* One query row, done the plain way.  s and w are scratch rows of length L. */
+/* One query row, done the plain way.  s and w are scratch rows of length Lk. */
 static void one_row(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                    int64_t L, int64_t n_q, int64_t n_kv, int64_t d_h,
-                    double scale, int causal, int64_t row,
-                    double *s, double *w, double *out, double *lse,
-                    uint64_t *flops)
+                    int64_t Lq, int64_t Lk, int64_t q_off, int64_t n_q,
+                    int64_t n_kv, int64_t d_h, double scale, int causal,
+                    int64_t row, double *s, double *w, double *out,
+                    double *lse, uint64_t *flops)
 {
+    const int64_t L = Lk;
     const int64_t g = n_q / n_kv;
-    const int64_t i = row % L;
-    const int64_t h = (row / L) % n_q;
-    const int64_t b = row / (L * n_q);
+    const int64_t i = row % Lq;
+    const int64_t h = (row / Lq) % n_q;
+    const int64_t b = row / (Lq * n_q);
     const int64_t kvh = h / g;
-    const uint16_t *qrow = q + ((b * n_q + h) * L + i) * d_h;
-    const uint16_t *kbase = k + (b * n_kv + kvh) * L * d_h;
-    const uint16_t *vbase = v + (b * n_kv + kvh) * L * d_h;
-    /* visible keys: j <= i when causal, all L keys otherwise */
-    const int64_t n_vis = causal ? i + 1 : L;
+    const uint16_t *qrow = q + ((b * n_q + h) * Lq + i) * d_h;
+    const uint16_t *kbase = k + (b * n_kv + kvh) * Lk * d_h;
+    const uint16_t *vbase = v + (b * n_kv + kvh) * Lk * d_h;
+    /* visible keys: j <= q_off + i when causal, all Lk keys otherwise */
+    const int64_t n_vis = causal ? q_off + i + 1 : Lk;
 
     /* 1. materialise the whole score row; masked entries are -inf and their
      *    dot products are never formed */
@@ -120,24 +127,27 @@ static void one_row(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 }
 
 /*
- * Attention for the requested rows.
- *   rows == NULL: every row, in flat order (n_rows must equal B*n_q*L).
+ * Attention of a chunk for the requested rows.
+ *   rows == NULL: every row, in flat order (n_rows must equal B*n_q*Lq).
+ *   q_off >= 0, and q_off + Lq <= Lk when causal (every query sees its own
+ *   position).
  *   out:  [n_rows, d_h] fp64, lse: [n_rows] fp64, flops: counted flops.
  *   threads <= 0 leaves the OpenMP default.
  * Returns ORACLE_OK, ORACLE_BAD_ARG or ORACLE_NO_MEMORY.
  */
-int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                     int64_t B, int64_t L, int64_t n_q, int64_t n_kv,
-                     int64_t d_h, float scale, int causal,
-                     const int64_t *rows, int64_t n_rows,
-                     double *out, double *lse, uint64_t *flops, int threads)
+int oracle_attn_rows_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           int64_t B, int64_t Lq, int64_t Lk, int64_t q_off,
+                           int64_t n_q, int64_t n_kv, int64_t d_h, float scale,
+                           int causal, const int64_t *rows, int64_t n_rows,
+                           double *out, double *lse, uint64_t *flops, int threads)
 {
     if (!q || !k || !v || !out || !lse || !flops) return ORACLE_BAD_ARG;
-    if (B < 1 || L < 1 || n_q < 1 || n_kv < 1 || d_h < 1) return ORACLE_BAD_ARG;
+    if (B < 1 || Lq < 1 || Lk < 1 || n_q < 1 || n_kv < 1 || d_h < 1) return ORACLE_BAD_ARG;
     if (n_q % n_kv != 0) return ORACLE_BAD_ARG;
     if (causal != 0 && causal != 1) return ORACLE_BAD_ARG;
+    if (q_off < 0 || (causal && q_off + Lq > Lk)) return ORACLE_BAD_ARG;
     if (!isfinite(scale)) return ORACLE_BAD_ARG;
-    const int64_t total_rows = B * n_q * L;
+    const int64_t total_rows = B * n_q * Lq;
     if (rows == NULL && n_rows != total_rows) return ORACLE_BAD_ARG;
     if (rows != NULL)
         for (int64_t r = 0; r < n_rows; ++r)
@@ -153,8 +163,8 @@ int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 #endif
 #pragma omp parallel reduction(+ : count) reduction(| : failed)
     {
-        double *s = (double *)malloc((size_t)L * sizeof(double));
-        double *w = (double *)malloc((size_t)L * sizeof(double));
+        double *s = (double *)malloc((size_t)Lk * sizeof(double));
+        double *w = (double *)malloc((size_t)Lk * sizeof(double));
         /* every thread reaches the work-sharing loop, even one whose scratch
          * allocation failed; such a thread only records the failure */
 #pragma omp for schedule(dynamic, 4)
@@ -164,7 +174,7 @@ int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 continue;
             }
             const int64_t row = rows ? rows[r] : r;
-            one_row(q, k, v, L, n_q, n_kv, d_h, sc, causal, row, s, w,
+            one_row(q, k, v, Lq, Lk, q_off, n_q, n_kv, d_h, sc, causal, row, s, w,
                     out + r * d_h, lse + r, &count);
         }
         free(s);
@@ -172,6 +182,18 @@ int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     }
     *flops = count;
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* Whole-sequence attention for the requested rows: the chunk with
+ * Lq = Lk = L and q_off = 0 (rows are (b * n_q + h) * L + i). */
+int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     int64_t B, int64_t L, int64_t n_q, int64_t n_kv,
+                     int64_t d_h, float scale, int causal,
+                     const int64_t *rows, int64_t n_rows,
+                     double *out, double *lse, uint64_t *flops, int threads)
+{
+    return oracle_attn_rows_chunk(q, k, v, B, L, L, 0, n_q, n_kv, d_h, scale, causal,
+                                  rows, n_rows, out, lse, flops, threads);
 }
 
 /* Number of OpenMP threads a parallel region would use (for reporting). */

@@ -42,12 +42,13 @@ def _random_case(B, L, n_q, n_kv, d, seed, mult=1.0):
 # section "The O(n^2) problem": softmax(Q K^T / sqrt d) V; causal: each token
 # sees itself and earlier tokens; GQA: head h reads kv-head h // g)
 # ----------------------------------------------------------------------------
-def _brute_force(q, k, v, scale, causal):
+def _brute_force(q, k, v, scale, causal, q_off=0):
+    """50-digit attention; query row i sits at key position q_off + i."""
     mpmath = pytest.importorskip("mpmath")
     mp = mpmath.mp
     mp.dps = 50
     B, n_q, L, d = q.shape
-    n_kv = k.shape[1]
+    n_kv, Lk = k.shape[1], k.shape[2]
     g = n_q // n_kv
     qv, kv_, vv = _vals(q), _vals(k), _vals(v)
     sc = mp.mpf(float(np.float32(scale)))
@@ -57,7 +58,7 @@ def _brute_force(q, k, v, scale, causal):
         for h in range(n_q):
             kh = h // g
             for i in range(L):
-                keys = range(i + 1) if causal else range(L)
+                keys = range(q_off + i + 1) if causal else range(Lk)
                 s = []
                 for j in keys:
                     acc = mp.mpf(0)
@@ -387,3 +388,136 @@ def test_bad_arguments_rejected():
         oracle.attention_rows(q, k, v, float("nan"), True)
     with pytest.raises(ValueError):
         oracle.attention_rows(q, k, v, 0.5, True, rows=np.array([8], dtype=np.int64))
+
+
+# ----------------------------------------------------------------------------
+# chunked prefill ("flops / prefill-attention", section "Workarounds": a long
+# prompt processed in pieces; a piece's query i is token q_off + i of the
+# sequence and, causally, sees every earlier token of the whole sequence)
+# ----------------------------------------------------------------------------
+def _random_chunk(B, Lq, Lk, n_q, n_kv, d, seed):
+    q, _, _ = inputs.make_qkv(B, Lq, n_q, n_kv, d, seed)
+    _, k, v = inputs.make_qkv(B, Lk, n_q, n_kv, d, seed + 1000)
+    return q, k, v
+
+
+CHUNK_TINY = [
+    # B, Lq, Lk, q_off, n_q, n_kv, d, causal, scale
+    (1, 3, 9, 6, 2, 1, 4, 1, 0.4),
+    (2, 4, 7, 2, 4, 2, 3, 1, 0.8),
+    (1, 1, 6, 5, 3, 1, 5, 1, 0.3),
+    (1, 5, 5, 0, 2, 2, 4, 1, 0.6),
+    (1, 4, 3, 0, 4, 2, 4, 0, 0.5),   # non-causal, fewer keys than queries
+    (2, 3, 8, 0, 2, 1, 6, 0, 1.1),
+]
+
+
+@pytest.mark.parametrize("B,Lq,Lk,q_off,n_q,n_kv,d,causal,scale", CHUNK_TINY)
+def test_chunk_brute_force_50_digits(B, Lq, Lk, q_off, n_q, n_kv, d, causal, scale):
+    q, k, v = _random_chunk(B, Lq, Lk, n_q, n_kv, d, seed=300 + Lq * Lk + q_off)
+    ref_o, ref_l = _brute_force(q, k, v, scale, causal, q_off=q_off)
+    o, l, f = oracle.attention_rows_chunk(q, k, v, scale, causal, q_offset=q_off)
+    assert np.max(np.abs(o - ref_o.reshape(-1, d))) <= 1e-14
+    assert np.max(np.abs(l - ref_l.reshape(-1))) <= 1e-14
+    vis = (q_off + np.arange(Lq) + 1) if causal else np.full(Lq, Lk)
+    assert f == 4 * d * B * n_q * int(vis.sum())
+
+
+def test_chunk_rows_are_rows_of_the_whole_sequence():
+    # the last Lq queries of a causal sequence of length L, run as a chunk at
+    # q_off = L - Lq over all L keys, are exactly those rows of the whole run
+    B, L, n_q, n_kv, d = 2, 70, 4, 2, 16
+    q, k, v = _random_case(B, L, n_q, n_kv, d, seed=71)
+    o, l, _ = oracle.attention_rows(q, k, v, 0.3, True)
+    o = o.reshape(B, n_q, L, d)
+    l = l.reshape(B, n_q, L)
+    for q_off in (0, 1, 31, 32, 69):
+        qc = np.ascontiguousarray(q[:, :, q_off:])
+        oc, lc, _ = oracle.attention_rows_chunk(qc, k, v, 0.3, True, q_offset=q_off)
+        assert np.array_equal(oc.reshape(B, n_q, L - q_off, d), o[:, :, q_off:])
+        assert np.array_equal(lc.reshape(B, n_q, L - q_off), l[:, :, q_off:])
+    # keys past the chunk's last query are invisible: a causal middle chunk
+    # reads only the prefix k[:, :, :q_off + Lq]
+    q_off, Lq = 20, 17
+    qc = np.ascontiguousarray(q[:, :, q_off:q_off + Lq])
+    oc, lc, _ = oracle.attention_rows_chunk(qc, k, v, 0.3, True, q_offset=q_off)
+    assert np.array_equal(oc.reshape(B, n_q, Lq, d), o[:, :, q_off:q_off + Lq])
+    kp = np.ascontiguousarray(k[:, :, :q_off + Lq])
+    vp = np.ascontiguousarray(v[:, :, :q_off + Lq])
+    op, lp, _ = oracle.attention_rows_chunk(qc, kp, vp, 0.3, True, q_offset=q_off)
+    assert np.array_equal(op, oc) and np.array_equal(lp, lc)
+
+
+def test_chunk_zero_query_running_mean():
+    # equal scores: row i of a causal chunk is the mean of V[0 .. q_off + i]
+    Lq, Lk, q_off, d = 6, 40, 30, 8
+    _, k, v = _random_chunk(1, Lq, Lk, 1, 1, d, seed=72)
+    q = np.zeros((1, 1, Lq, d), dtype=np.uint16)
+    o, l, _ = oracle.attention_rows_chunk(q, k, v, 0.5, True, q_offset=q_off)
+    n = q_off + np.arange(Lq) + 1
+    means = np.cumsum(_vals(v)[0, 0], axis=0)[q_off:q_off + Lq] / n[:, None]
+    assert np.max(np.abs(o - means)) <= 1e-14
+    assert np.max(np.abs(l - np.log(n))) <= 1e-14
+
+
+def test_chunk_bad_arguments_rejected():
+    q, k, v = _random_chunk(1, 4, 8, 2, 1, 4, seed=73)
+    with pytest.raises(ValueError):
+        oracle.attention_rows_chunk(q, k, v, 0.5, True, q_offset=5)   # 5 + 4 > 8
+    with pytest.raises(ValueError):
+        oracle.attention_rows_chunk(q, k, v, 0.5, True, q_offset=-1)
+    with pytest.raises(ValueError):
+        oracle.attention_rows_chunk(q, k, v, 0.5, False, q_offset=-1)
+    oracle.attention_rows_chunk(q, k, v, 0.5, False, q_offset=100)  # unused when not causal
+
+
+# ----------------------------------------------------------------------------
+# merging partial results ("Long-Context Attention Explained", section
+# "Online softmax": statistics of two key sets combine by rescaling both to
+# the larger maximum; the LSE carries max and sum in one number)
+# ----------------------------------------------------------------------------
+def test_merge_prefix_and_chunk_equals_whole_row():
+    # a chunk's causal attention over all keys = merge of (non-causal over the
+    # keys before the chunk) and (causal over the chunk's own keys)
+    B, Lq, q_off, n_q, n_kv, d = 2, 19, 45, 6, 2, 16
+    Lk = q_off + Lq
+    q, k, v = _random_chunk(B, Lq, Lk, n_q, n_kv, d, seed=74)
+    o, l, _ = oracle.attention_rows_chunk(q, k, v, 0.2, True, q_offset=q_off)
+    kp, vp = (np.ascontiguousarray(x[:, :, :q_off]) for x in (k, v))
+    ks, vs = (np.ascontiguousarray(x[:, :, q_off:]) for x in (k, v))
+    oa, la, _ = oracle.attention_rows_chunk(q, kp, vp, 0.2, False)
+    ob, lb, _ = oracle.attention_rows_chunk(q, ks, vs, 0.2, True, q_offset=0)
+    om, lm = oracle.merge_partials(oa, la, ob, lb)
+    assert np.max(np.abs(om - o)) <= 1e-14
+    assert np.max(np.abs(lm - l)) <= 1e-13
+    # the merge is symmetric
+    om2, lm2 = oracle.merge_partials(ob, lb, oa, la)
+    assert np.max(np.abs(om2 - om)) <= 1e-15 and np.array_equal(lm2, lm)
+
+
+def test_merge_closed_forms():
+    rng = np.random.default_rng(75)
+    o = rng.standard_normal((5, 8))
+    l = rng.standard_normal(5) * 10
+    # two copies of one partial: same output, LSE + ln 2
+    om, lm = oracle.merge_partials(o, l, o, l)
+    assert np.max(np.abs(om - o)) <= 1e-15
+    assert np.max(np.abs(lm - (l + math.log(2)))) <= 1e-14
+    # an empty side (LSE -inf) leaves the other exactly
+    ninf = np.full(5, -np.inf)
+    om, lm = oracle.merge_partials(o, l, np.full_like(o, np.nan), ninf)
+    assert np.array_equal(om, o) and np.array_equal(lm, l)
+    om, lm = oracle.merge_partials(np.zeros_like(o), ninf, o, l)
+    assert np.array_equal(om, o) and np.array_equal(lm, l)
+    # both empty: out 0, LSE -inf
+    om, lm = oracle.merge_partials(o, ninf, o, ninf)
+    assert np.array_equal(om, np.zeros_like(o)) and np.all(np.isneginf(lm))
+    # LSEs far apart (beyond exp's range) still weigh correctly
+    la = np.array([1000.0]); lb = np.array([0.0])
+    om, lm = oracle.merge_partials(o[:1], la, o[1:2], lb)
+    assert np.array_equal(om, o[:1]) and lm[0] == 1000.0
+    # weights e^1 : e^0 against a hand-worked value
+    om, lm = oracle.merge_partials(np.array([[1.0]]), np.array([1.0]),
+                                   np.array([[0.0]]), np.array([0.0]))
+    assert abs(om[0, 0] - math.e / (math.e + 1)) <= 1e-15
+    assert abs(lm[0] - math.log(math.e + 1)) <= 1e-15

@@ -21,8 +21,12 @@ SRC = open(obuild.SRC).read()
 
 MUTANTS = {
     "no max subtraction": ("w[j] = exp(s[j] - m);", "w[j] = exp(s[j]); (void)0;"),
-    "mask excludes self": ("causal ? i + 1 : L", "causal ? i : L"),
-    "mask one too wide": ("causal ? i + 1 : L", "causal ? (i + 2 < L ? i + 2 : L) : L"),
+    "mask excludes self": ("causal ? q_off + i + 1 : Lk", "causal ? q_off + i : Lk"),
+    "mask one too wide": ("causal ? q_off + i + 1 : Lk",
+                          "causal ? (q_off + i + 2 < Lk ? q_off + i + 2 : Lk) : Lk"),
+    "chunk offset ignored": ("causal ? q_off + i + 1 : Lk", "causal ? i + 1 : Lk"),
+    "kv heads strided by Lq": ("const uint16_t *kbase = k + (b * n_kv + kvh) * Lk * d_h;",
+                               "const uint16_t *kbase = k + (b * n_kv + kvh) * Lq * d_h;"),
     "kv head h mod n_kv": ("const int64_t kvh = h / g;", "const int64_t kvh = h % n_kv;"),
     "log2 in lse": ("*lse = m + log(total);", "*lse = m + log2(total);"),
     "K read transposed": ("dot += widen_bf16(qrow[t]) * widen_bf16(krow[t]);",
@@ -82,8 +86,20 @@ def _check_flops(lib):
     return fc == 2 * B * n_q * d * L * (L + 1)
 
 
+def _check_chunk_brute(lib):
+    # a causal chunk at an offset, GQA with two kv heads and two sequences,
+    # fewer queries than keys
+    B, Lq, Lk, q_off, n_q, n_kv, d = 2, 3, 8, 4, 4, 2, 4
+    q, _, _ = inputs.make_qkv(B, Lq, n_q, n_kv, d, seed=81)
+    _, k, v = inputs.make_qkv(B, Lk, n_q, n_kv, d, seed=82)
+    ref_o, ref_l = _brute_force(q, k, v, 0.5, 1, q_off=q_off)
+    o, l, _ = oracle.attention_rows_chunk(q, k, v, 0.5, True, q_offset=q_off, lib=lib)
+    return bool(np.max(np.abs(o - ref_o.reshape(-1, d))) <= 1e-14 and
+                np.max(np.abs(l - ref_l.reshape(-1))) <= 1e-14)
+
+
 CHECKS = [_check_brute, _check_large_scores, _check_constant_v,
-          _check_zero_query, _check_flops]
+          _check_zero_query, _check_flops, _check_chunk_brute]
 
 
 def _build_variant(tmp_path, name, src):
