@@ -19,6 +19,11 @@
 //  * Grouped-query heads: the query heads of one key/value head read the
 //    same K/V tile from LDS, so K and V bytes are amortised over the group
 //    ("flops / prefill-attention", section "Arithmetic intensity").
+//  * Chunked prefill: the queries may be a chunk sitting at an offset into a
+//    longer K/V (query row i at key position q_off + i, causal mask anchored
+//    there), and two partial results over disjoint key sets merge by their
+//    LSEs ("flops / prefill-attention", section "Workarounds"; "Long-Context
+//    Attention Explained", section "Online softmax").
 //
 // CDNA4 mapping:
 //  * A workgroup covers 256 query columns: HWG heads of one group times
@@ -46,10 +51,10 @@
 //    consecutive 16-bit values of row r and lane i receives column i of the
 //    four rows).
 //  * K and V tiles of 64 keys go from global memory straight into LDS
-//    (global_load_lds_dwordx4): three K buffers and two V buffers, one
-//    barrier per tile.  The compute runs in 32-key halves: the scores of the
-//    next half are formed on the MFMA pipe while the softmax of the current
-//    half is on the VALU, which needs K one tile ahead of V.
+//    (buffer loads with the LDS destination bit): a 4-tile ring each for K
+//    and V, tiles requested three ahead, one barrier per tile.  The compute
+//    runs in 32-key halves: the scores of the next half are formed on the
+//    MFMA pipe while the softmax of the current half is on the VALU.
 //  * LDS rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads
 //    do not collide on banks (see k_swz / v_swz).
 //  * exp is exp2 with scale*log2(e) folded into one FMA; l and acc are only
