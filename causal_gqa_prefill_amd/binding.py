@@ -46,6 +46,11 @@ def library():
                                                ctypes.c_float, ci, vp]
         lib.attn_merge_partials.restype = ci
         lib.attn_merge_partials.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_longlong, ci, vp]
+        lib.attn_decode_fwd.restype = ci
+        lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ctypes.c_longlong, ci, ci, ci,
+                                        ctypes.c_float, vp, ctypes.c_size_t, vp]
+        lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.attn_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
         lib.attn_prefill_strerror.restype = ctypes.c_char_p
         lib.attn_prefill_strerror.argtypes = [ci]
         lib.attn_prefill_version.restype = ci
@@ -84,6 +89,22 @@ def merge_raw(oa_ptr, la_ptr, ob_ptr, lb_ptr, out_ptr, lo_ptr, rows, d_h, stream
         ctypes.c_void_p(oa_ptr), ctypes.c_void_p(la_ptr), ctypes.c_void_p(ob_ptr),
         ctypes.c_void_p(lb_ptr), ctypes.c_void_p(out_ptr), ctypes.c_void_p(lo_ptr),
         int(rows), int(d_h), ctypes.c_void_p(stream_ptr))
+
+
+def decode_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, Lk, kv_capacity, n_q, n_kv, d_h, scale,
+               ws_ptr, ws_bytes, stream_ptr):
+    """Direct call of attn_decode_fwd with integer pointers; returns status."""
+    return library().attn_decode_fwd(
+        ctypes.c_void_p(q_ptr), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
+        ctypes.c_void_p(out_ptr), ctypes.c_void_p(lse_ptr), int(B), int(Lk), int(kv_capacity),
+        int(n_q), int(n_kv), int(d_h), float(scale), ctypes.c_void_p(ws_ptr), int(ws_bytes),
+        ctypes.c_void_p(stream_ptr))
+
+
+def decode_workspace_bytes(B, Lk, n_q, n_kv, d_h):
+    """Bytes of workspace attn_decode_fwd needs (0 for rejected sizes)."""
+    return int(library().attn_decode_workspace_bytes(int(B), int(Lk), int(n_q), int(n_kv),
+                                                     int(d_h)))
 
 
 def _check(q, k, v, same_length=True):
@@ -213,3 +234,58 @@ def merge_partials(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None):
     if status != ATTN_PREFILL_OK:
         raise AttnPrefillError(status, strerror(status))
     return out, lse_out
+
+
+def attn_decode_into(q, k, v, out, lse, Lk=None, scale=None, workspace=None, stream=None):
+    """Decode into caller-provided out (bf16 like q) and lse (fp32 [B, n_q]):
+    q bf16 [B, n_q, d_h], one query per sequence at position Lk - 1; k, v
+    bf16 [B, n_kv, capacity, d_h], of which the first Lk rows (default: all)
+    are read.  workspace: a contiguous device tensor of at least
+    decode_workspace_bytes(...) bytes, allocated here when None."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B, n_q, d_h]; k and v [B, n_kv, capacity, d_h], equal shapes")
+    B, n_q, d_h = q.shape
+    if k.shape[0] != B or k.shape[3] != d_h:
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if not (q.device == k.device == v.device) or q.device.type != "cuda":
+        raise ValueError("q, k and v must be on the same GPU")
+    n_kv, cap = k.shape[1], k.shape[2]
+    if Lk is None:
+        Lk = cap
+    if out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, n_q) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, n_q]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_h)
+    need = decode_workspace_bytes(B, Lk, n_q, n_kv, d_h)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        status = decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, Lk, cap, n_q, n_kv, d_h, scale,
+                            workspace.data_ptr(), ws_bytes, s.cuda_stream)
+    if status != ATTN_PREFILL_OK:
+        raise AttnPrefillError(status, strerror(status))
+    return out, lse
+
+
+def attn_decode(q, k, v, Lk=None, scale=None, workspace=None, stream=None):
+    """Decode attention: returns (out bf16 [B, n_q, d_h], lse fp32 [B, n_q])."""
+    import torch
+    out = torch.empty_like(q)
+    lse = torch.empty(tuple(q.shape[:2]), dtype=torch.float32, device=q.device)
+    return attn_decode_into(q, k, v, out, lse, Lk=Lk, scale=scale, workspace=workspace,
+                            stream=stream)

@@ -10,6 +10,11 @@ trained weights or activations are involved.
 Chunked-prefill workloads ("flops / prefill-attention", section
 "Workarounds": a long prompt prefilled in pieces) put a chunk of Lq queries
 at key position q_offset of a longer K/V; seed = 2000 + index.
+
+Decode workloads (one new token per sequence against its whole cache,
+"Memory-bound vs compute-bound", section "Prefill against decode") use the
+same geometries, batched at 8K and 32K context, and the 128K-token prompt of
+"Long-Context Attention Explained"; seed = 3000 + index.
 """
 from dataclasses import dataclass
 import math
@@ -112,3 +117,44 @@ CHUNK_CONFIGS = [
 
 def chunk_config(index: int) -> ChunkConfig:
     return CHUNK_CONFIGS[index - 1]
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    index: int
+    name: str
+    B: int
+    Lk: int
+    n_q: int
+    n_kv: int
+    d_h: int
+    sampled_rows: int = 0
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d_h)))
+
+    @property
+    def seed(self) -> int:
+        return 3000 + self.index
+
+    def kv_bytes(self) -> int:
+        return 2 * self.B * self.n_kv * self.Lk * self.d_h * 2
+
+    def describe(self) -> str:
+        return (f"{self.name}: B={self.B} Lk={self.Lk} n_q={self.n_q} n_kv={self.n_kv} "
+                f"d_h={self.d_h}")
+
+
+DECODE_CONFIGS = [
+    DecodeConfig(1, "Llama-3-8B-shaped GQA-4 decode, batch 32 at 8K context",
+                 32, 8192, 32, 8, 128, sampled_rows=256),
+    DecodeConfig(2, "synthetic wide GQA-6 decode after a 128K prompt",
+                 1, 131072, 36, 6, 128),
+    DecodeConfig(3, "Llama-2-70B-shaped GQA-8 decode, batch 8 at 32K context",
+                 8, 32768, 64, 8, 128, sampled_rows=256),
+]
+
+
+def decode_config(index: int) -> DecodeConfig:
+    return DECODE_CONFIGS[index - 1]

@@ -141,6 +141,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt lgkmcnt(0) alone: every LDS read of this wave has returned
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
 // Raw buffer resource over `bytes` bytes from `base`: loads at offsets past
 // the end return zeros (the hardware range check), so the last, partial
 // K/V tile needs no clamping.
@@ -671,6 +676,322 @@ __global__ __launch_bounds__(256) void merge_kernel(
   if (c8 == 0) lo[row] = sum > 0.0f ? m + __logf(sum) : -INFINITY;
 }
 
+// ---- decode: one new query per sequence against its whole K/V cache.  The
+// query is a single vector, so attention is a matrix-vector product against
+// the cache and its time is the cache bytes over the memory bandwidth
+// ("Memory-bound vs compute-bound", sections "Prefill against decode" and
+// "Attention itself"; "Long-Context Attention Explained", the paragraphs on
+// prefill against decode).
+//
+// decode_split_kernel: work item = (b, kv-head, key range).  Four waves per
+// workgroup; wave w streams the 64-key tiles w, w + 4, ... of the range
+// through its own 32 KB of LDS (K tile, V tile) with the same DMA loads,
+// swizzles and fragment reads as the prefill kernel, and forms the g query
+// heads of the group as the 32 columns of S^T = K Q^T (columns >= g hold
+// zero queries and are never stored).  The four waves' running states merge
+// in LDS at the end, and the workgroup writes one fp32 partial per query
+// head: O normalised by the range's own row sum, and the range's LSE.
+// decode_combine_kernel then merges the partials of each row by their LSEs
+// (the online-softmax combination, "Long-Context Attention Explained",
+// section "Online softmax").
+constexpr int kDecWaves = 4;
+constexpr int kDecMaxSplits = 4096;   // partials per row the combine stages in LDS
+
+template <int D>
+__global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
+    const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+    const unsigned short* __restrict__ v, float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    int Lk, long long kv_cap, int n_q, int n_kv, int n_split, int split_keys, float scale) {
+  constexpr int KSTEPS = D / 16;
+  constexpr int TBLK = D / 32;
+  constexpr int ROWB = 2 * D;
+  constexpr int TILE = kBC * ROWB;           // bytes of one 64-key K or V tile
+  constexpr int LOADS = TILE / 1024;         // 1 KB loads per tile, one wave
+  constexpr int WAVE_LDS = 2 * TILE;         // a wave's K tile then its V tile
+  static_assert(32 * D * 4 + 2 * 32 * 4 <= WAVE_LDS, "wave state must fit its LDS");
+
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kDecWaves * WAVE_LDS];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hi = lane >> 5;
+  const int col = lane & 31;
+  unsigned char* const wbuf = smem + wave * WAVE_LDS;
+  LDS_AS unsigned char* const wl = (LDS_AS unsigned char*)wbuf;
+
+  const int item = blockIdx.x;
+  const int split = item % n_split;
+  const int rest = item / n_split;
+  const int kvh = rest % n_kv;
+  const int b = rest / n_kv;
+  const int g = n_q / n_kv;
+  const int j_begin = split * split_keys;
+  const int j_end = min(Lk, j_begin + split_keys);
+  const unsigned short* kbase = k + ((size_t)b * n_kv + kvh) * (size_t)kv_cap * D;
+  const unsigned short* vbase = v + ((size_t)b * n_kv + kvh) * (size_t)kv_cap * D;
+
+  // Q^T as the B operand: column col is query head kvh * g + col
+  bf16x8 qf[KSTEPS];
+  {
+    const unsigned short* qrow = q + ((size_t)b * n_q + (size_t)kvh * g + col) * D;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (col < g) raw = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hi * 8);
+      qf[kk] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  // tile-load source offsets (the wave moves a whole tile: LOADS loads of
+  // 1 KB) and fragment read offsets, as in the prefill kernel
+  int k_src[LOADS], v_src[LOADS];
+#pragma unroll
+  for (int s = 0; s < LOADS; ++s) {
+    const int byte = s * 1024 + lane * 16;
+    const int row = byte / ROWB;
+    const int pos = (byte % ROWB) >> 4;
+    k_src[s] = row * ROWB + ((pos ^ k_swz<D>(row)) << 4);
+    v_src[s] = row * ROWB + ((pos ^ v_swz<D>(row)) << 4);
+  }
+  int k_rd[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk)
+    k_rd[kk] = col * ROWB + (((2 * kk + hi) ^ k_swz<D>(col)) << 4);
+  int v_rd[TBLK];
+  {
+    const int tr_r = (lane >> 2) & 3;
+    const int tr_q = lane & 3;
+    const int tr_g = (lane >> 4) & 1;
+#pragma unroll
+    for (int tb = 0; tb < TBLK; ++tb) {
+      const int t = 32 * tb + 16 * tr_g + 4 * tr_q;
+      const int key = 4 * hi + tr_r;
+      v_rd[tb] = TILE + key * ROWB + (((t >> 3) ^ v_swz<D>(key)) << 4) + ((t >> 2) & 1) * 8;
+    }
+  }
+
+  f32x16 acc[TBLK];
+#pragma unroll
+  for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[tb][r] = 0.0f;
+  float m_run = -INFINITY;   // log2 domain
+  float l_run = 0.0f;        // this lane's part of the row sum
+  const float c2 = scale * kLog2e;
+
+  for (int t0 = j_begin + wave * kBC; t0 < j_end; t0 += kDecWaves * kBC) {
+    wait_lgkm0();   // the previous tile's LDS reads are done before it is overwritten
+    dma_tile(kbase, k_src, LOADS, ROWB, t0, j_end, wbuf);
+    dma_tile(vbase, v_src, LOADS, ROWB, t0, j_end, wbuf + TILE);
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      const int j0 = t0 + 32 * jb;
+      if (j0 >= j_end) break;
+      bf16x8 kf[KSTEPS];
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        kf[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(wl + k_rd[kk] + jb * 32 * ROWB);
+      f32x16 sc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sc, 0, 0, 0);
+      // keys past the range are masked; j0 itself is always a key, so every
+      // column's max is finite
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + (r >> 2) * 8 + hi * 4 + (r & 3);
+        sc[r] = j < j_end ? sc[r] * c2 : -INFINITY;
+        mx = fmaxf(mx, sc[r]);
+      }
+      const float m_new = fmaxf(m_run, pair_max(mx));
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      bf16x8 pk[2];
+      float psum = 0.0f;
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(sc[half * 8 + e] - m_new);
+          psum += p;
+          pk[half][e] = (__bf16)p;
+        }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tb][r] *= alpha;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int tb = 0; tb < TBLK; ++tb) {
+          const LDS_AS unsigned char* base = wl + v_rd[tb] + (2 * jb + h) * 16 * ROWB;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base));
+          const s16x4 up =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base + 8 * ROWB));
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                              __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]});
+          acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[h], acc[tb], 0, 0, 0);
+        }
+    }
+  }
+
+  // ---- merge the four waves' states in LDS: wave w leaves m[32], l[32]
+  // and its unnormalised O as [32 columns][D] fp32 in its own LDS
+  const float l_tot = pair_sum(l_run);
+  __syncthreads();   // every wave is past its last LDS read and tile load
+  {
+    float* st = reinterpret_cast<float*>(wbuf);
+    float* acc_out = st + 64;
+    if (hi == 0) {
+      st[col] = m_run;
+      st[32 + col] = l_tot;
+    }
+#pragma unroll
+    for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        float4 o4;
+        o4.x = acc[tb][grp * 4 + 0];
+        o4.y = acc[tb][grp * 4 + 1];
+        o4.z = acc[tb][grp * 4 + 2];
+        o4.w = acc[tb][grp * 4 + 3];
+        *reinterpret_cast<float4*>(acc_out + col * D + 32 * tb + 8 * grp + 4 * hi) = o4;
+      }
+  }
+  __syncthreads();
+  // thread e of the workgroup takes elements e, e + 256, ... of [g][D]
+  for (int e = tid; e < g * D; e += 64 * kDecWaves) {
+    const int c = e / D;
+    const int d = e % D;
+    float mw[kDecWaves];
+    float m_all = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      mw[w] = reinterpret_cast<const float*>(smem + w * WAVE_LDS)[c];
+      m_all = fmaxf(m_all, mw[w]);
+    }
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float* st = reinterpret_cast<const float*>(smem + w * WAVE_LDS);
+      // a wave without a tile has m = -inf, l = 0 and O = 0: weight 0
+      const float f = __builtin_amdgcn_exp2f(mw[w] - m_all);
+      den += f * st[32 + c];
+      num += f * st[64 + c * D + d];
+    }
+    const size_t prow = ((size_t)b * n_q + (size_t)kvh * g + c) * n_split + split;
+    ws_o[prow * D + d] = num / den;
+    if (d == 0) ws_lse[prow] = (m_all + __log2f(den)) * kLn2;
+  }
+}
+
+// decode_combine_kernel: one workgroup of 256 threads per query row merges
+// the row's n_split fp32 partials by their LSEs: M = max lse, w_s =
+// exp(lse_s - M), O = sum w_s o_s / sum w_s (rounded once to bf16),
+// LSE = M + ln sum w_s.
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
+    unsigned short* __restrict__ out, float* __restrict__ lse, int n_split) {
+  constexpr int C4 = D / 4;            // float4 columns of a row
+  constexpr int SG = 256 / C4;         // split groups
+  __shared__ float w_s[kDecMaxSplits];
+  __shared__ float red[8];
+  __shared__ float4 part[SG][C4];
+  const int tid = threadIdx.x;
+  const size_t row = blockIdx.x;
+  const float* lrow = ws_lse + row * n_split;
+  const float* orow = ws_o + row * n_split * D;
+
+  // M: strided max, then across the wave (butterfly) and the four waves
+  float m = -INFINITY;
+  for (int s = tid; s < n_split; s += 256) {
+    const float x = lrow[s];
+    w_s[s] = x;
+    m = fmaxf(m, x);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // weights and their sum
+  float wsum = 0.0f;
+  for (int s = tid; s < n_split; s += 256) {
+    const float w = __expf(w_s[s] - m);
+    w_s[s] = w;
+    wsum += w;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+  if ((tid & 63) == 0) red[4 + (tid >> 6)] = wsum;
+  __syncthreads();
+  wsum = (red[4] + red[5]) + (red[6] + red[7]);
+  // weighted sum of the partial outputs: thread (sg, c4) takes splits sg, sg + SG, ...
+  const int c4 = tid % C4;
+  const int sg = tid / C4;
+  float4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+  for (int s = sg; s < n_split; s += SG) {
+    const float w = w_s[s];
+    const float4 o = *reinterpret_cast<const float4*>(orow + (size_t)s * D + 4 * c4);
+    a.x += w * o.x;
+    a.y += w * o.y;
+    a.z += w * o.z;
+    a.w += w * o.w;
+  }
+  part[sg][c4] = a;
+  __syncthreads();
+  if (tid < C4) {
+    float4 t = part[0][tid];
+    for (int g2 = 1; g2 < SG; ++g2) {
+      const float4 u = part[g2][tid];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+    }
+    const float inv = 1.0f / wsum;
+    bf16x4 y;
+    y[0] = (__bf16)(t.x * inv);
+    y[1] = (__bf16)(t.y * inv);
+    y[2] = (__bf16)(t.z * inv);
+    y[3] = (__bf16)(t.w * inv);
+    *reinterpret_cast<u32x2*>(out + row * D + 4 * tid) = __builtin_bit_cast(u32x2, y);
+    if (tid == 0) lse[row] = m + __logf(wsum);
+  }
+}
+
+// Key ranges of a decode call: enough work items to give every CU several
+// (a multiple of 256 keys per range, so each of the four waves gets whole
+// tiles), and never more than kDecMaxSplits ranges per row.
+struct DecodeSplit {
+  int n_split, split_keys;
+};
+DecodeSplit decode_split(int B, int Lk, int n_kv) {
+  const long long pairs = (long long)B * n_kv;
+  const long long target = 1024;   // about four workgroups per CU
+  long long want = (target + pairs - 1) / pairs;
+  const long long max_by_keys = ((long long)Lk + 255) / 256;
+  if (want > max_by_keys) want = max_by_keys;
+  if (want < 1) want = 1;
+  long long per = ((long long)Lk + want - 1) / want;
+  per = (per + 255) / 256 * 256;
+  long long n = ((long long)Lk + per - 1) / per;
+  if (n > kDecMaxSplits) {
+    per = ((long long)Lk + kDecMaxSplits - 1) / kDecMaxSplits;
+    per = (per + 255) / 256 * 256;
+    n = ((long long)Lk + per - 1) / per;
+  }
+  return DecodeSplit{(int)n, (int)per};
+}
+
 }  // namespace
 
 extern "C" int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out,
@@ -720,6 +1041,85 @@ extern "C" int attn_merge_partials(const void* o_a, const float* lse_a, const vo
   return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
 }
 
+extern "C" size_t attn_decode_workspace_bytes(int B, int Lk, int n_q, int n_kv, int d_h) {
+  if (B < 1 || Lk < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return 0;
+  if (n_q / n_kv > 32 || Lk > INT_MAX - 4096) return 0;
+  if (d_h != 64 && d_h != 128) return 0;
+  const DecodeSplit sp = decode_split(B, Lk, n_kv);
+  size_t rows;
+  if (__builtin_mul_overflow((size_t)B, (size_t)n_q, &rows) ||
+      __builtin_mul_overflow(rows, (size_t)sp.n_split, &rows))
+    return 0;
+  // fp32 partial outputs [rows][d_h], then fp32 partial LSEs [rows]
+  size_t bytes;
+  if (__builtin_mul_overflow(rows, (size_t)(d_h + 1) * 4, &bytes)) return 0;
+  return bytes;
+}
+
+extern "C" int attn_decode_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                               int B, int Lk, long long kv_capacity, int n_q, int n_kv, int d_h,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  if (!q || !k || !v || !out || !lse || !workspace) return ATTN_PREFILL_ERR_NULL_PTR;
+  if (B < 1 || Lk < 1 || n_q < 1 || n_kv < 1) return ATTN_PREFILL_ERR_BAD_SHAPE;
+  if (kv_capacity < Lk) return ATTN_PREFILL_ERR_BAD_OFFSET;
+  if (Lk > INT_MAX - 4096) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;  // key indices stay in int
+  if (n_q % n_kv != 0) return ATTN_PREFILL_ERR_BAD_GQA;
+  if (n_q / n_kv > 32) return ATTN_PREFILL_ERR_UNSUPPORTED;
+  if (d_h != 64 && d_h != 128) return ATTN_PREFILL_ERR_BAD_HEADDIM;
+  if (!std::isfinite(scale)) return ATTN_PREFILL_ERR_BAD_SCALE;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                          reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out) |
+                          reinterpret_cast<uintptr_t>(workspace);
+  if ((align & 15) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3) != 0)
+    return ATTN_PREFILL_ERR_MISALIGNED;
+  size_t q_elems, kv_elems;
+  if (__builtin_mul_overflow((size_t)B, (size_t)n_q, &q_elems) ||
+      __builtin_mul_overflow(q_elems, (size_t)d_h, &q_elems) ||
+      __builtin_mul_overflow((size_t)B, (size_t)n_kv, &kv_elems) ||
+      __builtin_mul_overflow(kv_elems, (size_t)kv_capacity, &kv_elems) ||
+      __builtin_mul_overflow(kv_elems, (size_t)d_h, &kv_elems) ||
+      q_elems > ((size_t)1 << 61) || kv_elems > ((size_t)1 << 61))
+    return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  const size_t need = attn_decode_workspace_bytes(B, Lk, n_q, n_kv, d_h);
+  if (need == 0) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  if (workspace_bytes < need) return ATTN_PREFILL_ERR_WORKSPACE;
+  const DecodeSplit sp = decode_split(B, Lk, n_kv);
+  const long long grid = (long long)B * n_kv * sp.n_split;
+  const long long rows = (long long)B * n_q;
+  if (grid > INT_MAX || rows > INT_MAX) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  const size_t qb = q_elems * 2, kvb = kv_elems * 2, lb = (size_t)B * n_q * 4;
+  if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kvb) || overlaps(out, qb, v, kvb) ||
+      overlaps(out, qb, lse, lb) || overlaps(out, qb, workspace, need) ||
+      overlaps(lse, lb, q, qb) || overlaps(lse, lb, k, kvb) || overlaps(lse, lb, v, kvb) ||
+      overlaps(lse, lb, workspace, need) || overlaps(workspace, need, q, qb) ||
+      overlaps(workspace, need, k, kvb) || overlaps(workspace, need, v, kvb))
+    return ATTN_PREFILL_ERR_ALIASING;
+
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_lse = ws_o + (size_t)rows * sp.n_split * d_h;
+  const unsigned short* qs = static_cast<const unsigned short*>(q);
+  const unsigned short* ks = static_cast<const unsigned short*>(k);
+  const unsigned short* vs = static_cast<const unsigned short*>(v);
+  unsigned short* os = static_cast<unsigned short*>(out);
+  if (d_h == 128) {
+    hipLaunchKernelGGL(decode_split_kernel<128>, dim3((unsigned)grid), dim3(64 * kDecWaves), 0,
+                       stream, qs, ks, vs, ws_o, ws_lse, Lk, kv_capacity, n_q, n_kv, sp.n_split,
+                       sp.split_keys, scale);
+    if (hipGetLastError() != hipSuccess) return ATTN_PREFILL_ERR_LAUNCH;
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)rows), dim3(256), 0, stream,
+                       ws_o, ws_lse, os, lse, sp.n_split);
+  } else {
+    hipLaunchKernelGGL(decode_split_kernel<64>, dim3((unsigned)grid), dim3(64 * kDecWaves), 0,
+                       stream, qs, ks, vs, ws_o, ws_lse, Lk, kv_capacity, n_q, n_kv, sp.n_split,
+                       sp.split_keys, scale);
+    if (hipGetLastError() != hipSuccess) return ATTN_PREFILL_ERR_LAUNCH;
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)rows), dim3(256), 0, stream,
+                       ws_o, ws_lse, os, lse, sp.n_split);
+  }
+  return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
+}
+
 extern "C" const char* attn_prefill_strerror(int status) {
   switch (status) {
     case ATTN_PREFILL_OK: return "success";
@@ -735,9 +1135,13 @@ extern "C" const char* attn_prefill_strerror(int status) {
     case ATTN_PREFILL_ERR_ALIASING: return "out or lse overlaps another buffer";
     case ATTN_PREFILL_ERR_LAUNCH: return "HIP kernel launch failed";
     case ATTN_PREFILL_ERR_BAD_OFFSET:
-      return "q_offset must be >= 0, and q_offset + Lq <= Lk when causal";
+      return "q_offset must be >= 0, q_offset + Lq <= Lk when causal, and kv_capacity >= Lk";
+    case ATTN_PREFILL_ERR_UNSUPPORTED:
+      return "decode supports at most 32 query heads per key/value head";
+    case ATTN_PREFILL_ERR_WORKSPACE:
+      return "workspace_bytes is smaller than attn_decode_workspace_bytes() for these sizes";
     default: return "unknown status";
   }
 }
 
-extern "C" int attn_prefill_version(void) { return 200; }
+extern "C" int attn_prefill_version(void) { return 300; }

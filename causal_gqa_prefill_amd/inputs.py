@@ -57,6 +57,21 @@ def make_chunk_qkv(B, Lq, Lk, n_q, n_kv, d_h, seed):
     return tuple(out)
 
 
+def make_decode_qkv(B, Lk, n_q, n_kv, d_h, seed, capacity=None):
+    """One query per sequence, Q [B,n_q,d_h], and its K/V cache
+    [B,n_kv,capacity,d_h] (capacity >= Lk; rows past Lk are drawn too, as
+    a stale cache would hold data), bf16 bits from N(0, 1), drawn in the
+    order Q, K, V from one stream."""
+    cap = Lk if capacity is None else capacity
+    rng = np.random.default_rng(seed)
+    out = [bf16_bits(rng.standard_normal((B, n_q, d_h), dtype=np.float32))]
+    for _ in range(2):
+        x = rng.standard_normal((B, n_kv, cap, d_h), dtype=np.float32)
+        out.append(bf16_bits(x))
+        del x
+    return tuple(out)
+
+
 def make_partials(rows, d_h, seed, empty_every=0):
     """Two partial results to merge: o_a, o_b bf16 bits [rows, d_h] from
     N(0, 1) and lse_a, lse_b float32 [rows] from 8 * N(0, 1) (so the two

@@ -83,3 +83,11 @@ def merge_bytes(rows, d_h, elem=2):
     """Bytes of one merge: read two [rows, d_h] partials and two fp32 LSE
     rows, write one of each."""
     return 3 * rows * d_h * elem + 3 * rows * 4
+
+
+def decode_bytes(B, Lk, n_q, n_kv, d_h, elem=2):
+    """Compulsory HBM bytes of one decode step: the whole K/V cache of Lk
+    rows, the query, the output and the fp32 LSE ("Memory-bound vs
+    compute-bound", section "Arithmetic intensity of a decoder step": the
+    K/V cache term)."""
+    return kv_bytes(B, Lk, n_kv, d_h, elem) + 2 * B * n_q * d_h * elem + 4 * B * n_q

@@ -70,8 +70,12 @@ enum attn_prefill_status {
     ATTN_PREFILL_ERR_SIZE_OVERFLOW = 8, /* a size or the grid overflows        */
     ATTN_PREFILL_ERR_ALIASING = 9,      /* out or lse overlaps another buffer  */
     ATTN_PREFILL_ERR_LAUNCH = 10,       /* the HIP launch failed               */
-    ATTN_PREFILL_ERR_BAD_OFFSET = 11    /* q_offset < 0, or (causal)
-                                           q_offset + Lq > Lk                  */
+    ATTN_PREFILL_ERR_BAD_OFFSET = 11,   /* q_offset < 0, or (causal)
+                                           q_offset + Lq > Lk, or (decode)
+                                           kv_capacity < Lk                    */
+    ATTN_PREFILL_ERR_UNSUPPORTED = 12,  /* (decode) more than 32 query heads
+                                           per key/value head                  */
+    ATTN_PREFILL_ERR_WORKSPACE = 13     /* (decode) workspace_bytes too small  */
 };
 
 /*
@@ -132,6 +136,43 @@ int attn_prefill_fwd_chunk(const void *q, const void *k, const void *v, void *ou
 int attn_merge_partials(const void *o_a, const float *lse_a, const void *o_b,
                         const float *lse_b, void *out, float *lse_out, long long rows,
                         int d_h, hipStream_t stream);
+
+/*
+ * Decode: one new query per sequence against the sequence's whole K/V cache.
+ * The query is token Lk - 1 of its sequence, its own key and value already in
+ * the cache, so it sees every cached key; attention becomes a matrix-vector
+ * product against the cache and its cost is reading the cache
+ * ("Memory-bound vs compute-bound", sections "Prefill against decode" and
+ * "Attention itself"; "Long-Context Attention Explained", the paragraphs on
+ * prefill against decode).  The
+ * result is the chunked prefill of one query at q_offset = Lk - 1.
+ *   q, out : device pointers, bf16 [B, n_q, d_h] (one token per sequence)
+ *   k, v   : device pointers, bf16 [B, n_kv, kv_capacity, d_h]: the cache,
+ *            of which rows 0 .. Lk - 1 of each (b, kv-head) are read
+ *   lse    : device pointer, fp32 [B, n_q]
+ *   Lk >= 1 keys, kv_capacity >= Lk rows allocated per (b, kv-head);
+ *   n_q % n_kv == 0 with at most 32 query heads per key/value head;
+ *   d_h in {64, 128}; scale any finite value.
+ *   workspace : device pointer, 16-byte aligned, at least
+ *               attn_decode_workspace_bytes(B, Lk, n_q, n_kv, d_h) bytes,
+ *               owned by the caller; it holds fp32 partial results of key
+ *               ranges between the two kernels of a call, so two calls that
+ *               share a workspace must be ordered (same stream).  Its
+ *               contents need no initialisation and are garbage afterwards.
+ * Numerics: Q K^T and P V as in attn_prefill_fwd; the partial results of the
+ * key ranges stay in fp32 and merge by their LSEs, O is rounded to bf16 once.
+ * out, lse and workspace may not overlap each other or any input.  Errors as
+ * for attn_prefill_fwd, plus ATTN_PREFILL_ERR_BAD_OFFSET (kv_capacity < Lk),
+ * ATTN_PREFILL_ERR_UNSUPPORTED and ATTN_PREFILL_ERR_WORKSPACE.
+ */
+int attn_decode_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+                    int B, int Lk, long long kv_capacity, int n_q, int n_kv, int d_h,
+                    float scale, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* Workspace bytes attn_decode_fwd needs for these sizes; 0 for sizes it
+ * rejects (or whose workspace size overflows). */
+size_t attn_decode_workspace_bytes(int B, int Lk, int n_q, int n_kv, int d_h);
 
 /* Static text for a status code (never NULL). */
 const char *attn_prefill_strerror(int status);

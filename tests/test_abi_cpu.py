@@ -22,15 +22,16 @@ def _declared_functions():
 def test_library_exports_header_symbols():
     lib = binding.library()
     names = _declared_functions()
-    assert names == ["attn_merge_partials", "attn_prefill_fwd", "attn_prefill_fwd_chunk",
-                     "attn_prefill_strerror", "attn_prefill_version"]
+    assert names == ["attn_decode_fwd", "attn_decode_workspace_bytes", "attn_merge_partials",
+                     "attn_prefill_fwd", "attn_prefill_fwd_chunk", "attn_prefill_strerror",
+                     "attn_prefill_version"]
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_strerror():
-    assert binding.library().attn_prefill_version() >= 200
-    for code in range(0, 12):
+    assert binding.library().attn_prefill_version() >= 300
+    for code in range(0, 14):
         assert binding.strerror(code) not in ("", "unknown status")
     assert binding.strerror(99) == "unknown status"
 
@@ -112,3 +113,57 @@ def test_merge_inputs_may_overlap_each_other():
     # at the launch, which needs a GPU, so check it passes validation by making
     # the aliasing check the last gate: a misaligned out still reports 7 first
     assert _call_merge(ob=ALIGNED, lb=ALIGNED + 0x10000000, out=ALIGNED + 0x40000002) == 7
+
+
+def _ws_splits(B, Lk, n_q, n_kv, d):
+    n = binding.decode_workspace_bytes(B, Lk, n_q, n_kv, d)
+    per_split = 4 * (d + 1) * B * n_q
+    assert n > 0 and n % per_split == 0
+    return n // per_split
+
+
+@pytest.mark.parametrize("B,Lk,n_q,n_kv,d", [(1, 1, 4, 4, 64), (1, 255, 8, 2, 128),
+                                             (1, 257, 8, 2, 128), (1, 32768, 32, 8, 128),
+                                             (1, 131072, 36, 6, 128), (32, 8192, 32, 8, 128),
+                                             (300, 100, 4, 1, 64), (1, 1 << 28, 8, 1, 128)])
+def test_decode_workspace_splits(B, Lk, n_q, n_kv, d):
+    # key ranges of 256-key multiples: at least one, every one non-empty, at
+    # most 4096 per row
+    n = _ws_splits(B, Lk, n_q, n_kv, d)
+    assert 1 <= n <= min(4096, (Lk + 255) // 256)
+    per = -(-Lk // n)
+    per = -(-per // 256) * 256
+    assert (n - 1) * per < Lk <= n * per
+
+
+@pytest.mark.parametrize("args", [(0, 10, 4, 4, 64), (1, 0, 4, 4, 64), (1, 10, 6, 4, 64),
+                                  (1, 10, 4, 4, 96), (1, 10, 66, 2, 64), (1, (1 << 31) - 1, 4, 4, 64)])
+def test_decode_workspace_rejects(args):
+    assert binding.decode_workspace_bytes(*args) == 0
+
+
+def _call_decode(**kw):
+    ws = binding.decode_workspace_bytes(2, 100, 8, 2, 128)
+    args = dict(q=ALIGNED, k=ALIGNED + 0x10000000, v=ALIGNED + 0x20000000,
+                out=ALIGNED + 0x30000000, lse=ALIGNED + 0x40000000, B=2, Lk=100, cap=128,
+                n_q=8, n_kv=2, d_h=128, scale=0.125, ws=ALIGNED + 0x50000000, ws_bytes=ws,
+                stream=0)
+    args.update(kw)
+    return binding.decode_raw(args["q"], args["k"], args["v"], args["out"], args["lse"],
+                              args["B"], args["Lk"], args["cap"], args["n_q"], args["n_kv"],
+                              args["d_h"], args["scale"], args["ws"], args["ws_bytes"],
+                              args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(ws=0), 1),
+    (dict(B=0), 2), (dict(Lk=0), 2),
+    (dict(n_q=7), 3), (dict(n_q=66), 12), (dict(d_h=80), 4), (dict(scale=float("nan")), 5),
+    (dict(cap=99), 11),
+    (dict(ws=ALIGNED + 0x50000008), 7), (dict(lse=ALIGNED + 0x40000002), 7),
+    (dict(ws_bytes=16), 13),
+    (dict(out=ALIGNED + 0x10000000 + 512), 9), (dict(ws=ALIGNED + 0x20000000 + 4096), 9),
+    (dict(lse=ALIGNED + 0x50000000 + 64), 9),
+])
+def test_decode_bad_arguments_rejected_on_host(kw, code):
+    assert _call_decode(**kw) == code

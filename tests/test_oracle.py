@@ -521,3 +521,23 @@ def test_merge_closed_forms():
                                    np.array([[0.0]]), np.array([0.0]))
     assert abs(om[0, 0] - math.e / (math.e + 1)) <= 1e-15
     assert abs(lm[0] - math.log(math.e + 1)) <= 1e-15
+
+
+# ----------------------------------------------------------------------------
+# decode ("Memory-bound vs compute-bound", sections "Prefill against decode"
+# and "Attention itself": one new query against the whole cache): the query is
+# token Lk - 1, so the chunk oracle with one query at q_offset = Lk - 1 is the
+# decode; it sees every cached key, i.e. it is the non-causal single row
+# ----------------------------------------------------------------------------
+def test_decode_reading_of_the_chunk_oracle():
+    B, Lk, n_q, n_kv, d = 2, 77, 6, 2, 16
+    q, k, v = _random_chunk(B, 1, Lk, n_q, n_kv, d, seed=76)
+    oc, lc, fc = oracle.attention_rows_chunk(q, k, v, 0.3, True, q_offset=Lk - 1)
+    on, ln_, fn = oracle.attention_rows_chunk(q, k, v, 0.3, False)
+    assert np.array_equal(oc, on) and np.array_equal(lc, ln_) and fc == fn == 4 * d * Lk * B * n_q
+    # and it is the last row of a whole-sequence prefill whose last query is q
+    qs = np.concatenate([np.zeros((B, n_q, Lk - 1, d), np.uint16), q], axis=2)
+    ow, lw, _ = oracle.attention_rows(np.ascontiguousarray(qs), k, v, 0.3, True)
+    ow = ow.reshape(B, n_q, Lk, d)[:, :, -1].reshape(-1, d)
+    lw = lw.reshape(B, n_q, Lk)[:, :, -1].reshape(-1)
+    assert np.array_equal(ow, oc) and np.array_equal(lw, lc)
