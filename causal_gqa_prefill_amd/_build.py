@@ -4,7 +4,8 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "attn_prefill.hip")
+SRCS = [os.path.join(PKG, "csrc", "attn_prefill.hip"), os.path.join(PKG, "csrc", "attn_fp8.hip")]
+SRC = SRCS[0]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_prefill.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -26,7 +27,7 @@ FLAGS = [
 def build(verbose: bool = False, extra=()) -> str:
     """Compile the HIP sources into LIB (always recompiles)."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -46,6 +46,10 @@ def library():
                                                ctypes.c_float, ci, vp]
         lib.attn_merge_partials.restype = ci
         lib.attn_merge_partials.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_longlong, ci, vp]
+        lib.attn_prefill_fwd_fp8.restype = ci
+        lib.attn_prefill_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci,
+                                             ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                             ctypes.c_float, ci, vp]
         lib.attn_decode_fwd.restype = ci
         lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ctypes.c_longlong, ci, ci, ci,
                                         ctypes.c_float, vp, ctypes.c_size_t, vp]
@@ -89,6 +93,16 @@ def merge_raw(oa_ptr, la_ptr, ob_ptr, lb_ptr, out_ptr, lo_ptr, rows, d_h, stream
         ctypes.c_void_p(oa_ptr), ctypes.c_void_p(la_ptr), ctypes.c_void_p(ob_ptr),
         ctypes.c_void_p(lb_ptr), ctypes.c_void_p(out_ptr), ctypes.c_void_p(lo_ptr),
         int(rows), int(d_h), ctypes.c_void_p(stream_ptr))
+
+
+def fwd_fp8_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, Lq, Lk, q_offset, n_q, n_kv, d_h,
+                scale, descale_q, descale_k, descale_v, causal, stream_ptr):
+    """Direct call of attn_prefill_fwd_fp8 with integer pointers; returns status."""
+    return library().attn_prefill_fwd_fp8(
+        ctypes.c_void_p(q_ptr), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
+        ctypes.c_void_p(out_ptr), ctypes.c_void_p(lse_ptr), int(B), int(Lq), int(Lk),
+        int(q_offset), int(n_q), int(n_kv), int(d_h), float(scale), float(descale_q),
+        float(descale_k), float(descale_v), int(causal), ctypes.c_void_p(stream_ptr))
 
 
 def decode_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, Lk, kv_capacity, n_q, n_kv, d_h, scale,
@@ -289,3 +303,57 @@ def attn_decode(q, k, v, Lk=None, scale=None, workspace=None, stream=None):
     lse = torch.empty(tuple(q.shape[:2]), dtype=torch.float32, device=q.device)
     return attn_decode_into(q, k, v, out, lse, Lk=Lk, scale=scale, workspace=workspace,
                             stream=stream)
+
+
+def _check_fp8(q, k, v):
+    import torch
+    byte_types = (torch.uint8, torch.float8_e4m3fn)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype not in byte_types:
+            raise TypeError(f"{name} must hold e4m3 codes (uint8 or float8_e4m3fn), got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, heads, L, d_h]")
+    if not (q.device == k.device == v.device) or q.device.type != "cuda":
+        raise ValueError("q, k and v must be on the same GPU")
+    B, n_q, Lq, d_h = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d_h:
+        raise ValueError(f"k and v must be [B, n_kv, Lk, d_h] matching q {tuple(q.shape)}; "
+                         f"got k {tuple(k.shape)}, v {tuple(v.shape)}")
+    return B, n_q, k.shape[1], Lq, k.shape[2], d_h
+
+
+def attn_prefill_fp8_into(q, k, v, out, lse, descale_q, descale_k, descale_v, q_offset=0,
+                          scale=None, causal=True, stream=None):
+    """FP8 prefill (see attn_prefill_fwd_fp8) into caller-provided out (bf16
+    [B, n_q, Lq, d_h]) and lse (fp32 [B, n_q, Lq]); q, k, v hold e4m3 codes."""
+    import torch
+    B, n_q, n_kv, Lq, Lk, d_h = _check_fp8(q, k, v)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, n_q, Lq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, n_q, Lq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_h)
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        status = fwd_fp8_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, Lq, Lk, q_offset, n_q, n_kv, d_h, scale,
+                             descale_q, descale_k, descale_v, int(bool(causal)), s.cuda_stream)
+    if status != ATTN_PREFILL_OK:
+        raise AttnPrefillError(status, strerror(status))
+    return out, lse
+
+
+def attn_prefill_fp8(q, k, v, descale_q, descale_k, descale_v, q_offset=0, scale=None,
+                     causal=True, stream=None):
+    """FP8 prefill: returns (out bf16 [B, n_q, Lq, d_h], lse fp32 [B, n_q, Lq])."""
+    import torch
+    B, n_q, _, Lq, _, d_h = _check_fp8(q, k, v)
+    out = torch.empty((B, n_q, Lq, d_h), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, n_q, Lq), dtype=torch.float32, device=q.device)
+    return attn_prefill_fp8_into(q, k, v, out, lse, descale_q, descale_k, descale_v,
+                                 q_offset=q_offset, scale=scale, causal=causal, stream=stream)

@@ -70,18 +70,9 @@
 #include <cstdint>
 
 #include "attn_prefill.h"
-
-#define LDS_AS __attribute__((address_space(3)))
+#include "device_common.h"
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 #ifndef ATTN_BLOCKS_PER_WAVE
 #define ATTN_BLOCKS_PER_WAVE 1
@@ -91,8 +82,6 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBlocksPerWave = ATTN_BLOCKS_PER_WAVE;
 constexpr int kCols = 256;            // query columns (head, row) per workgroup
 constexpr int kBC = 64;               // keys per K/V tile
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;        // rescale only past 2^8 growth
 
 // 16-byte chunk swizzles of the K and V tiles (row = key inside the tile).
@@ -111,64 +100,6 @@ __device__ __forceinline__ int k_swz(int row) {
 template <int D>
 __device__ __forceinline__ int v_swz(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
-}
-
-// max / sum of x over lanes l and l ^ 32
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Workgroup barrier that does not wait for outstanding memory operations
-// (the caller waits for exactly the loads the next tile needs); the signal
-// fences keep the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void tile_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// s_waitcnt with only a vector-memory count (expcnt and lgkmcnt at maximum)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// s_waitcnt lgkmcnt(0) alone: every LDS read of this wave has returned
-__device__ __forceinline__ void wait_lgkm0() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-}
-
-// Raw buffer resource over `bytes` bytes from `base`: loads at offsets past
-// the end return zeros (the hardware range check), so the last, partial
-// K/V tile needs no clamping.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-// One wave's share of a K or V tile load, global -> LDS: `loads` loads of
-// 1 KB, lane i of load s bringing the 16 bytes at source offset src[s]
-// (relative to row j0 of rows of `row_bytes`) to LDS byte dst + 1 KB s + 16 i.
-// A tile at or past row L reads as zeros and touches no memory.  The range
-// covers at most one tile, so it fits the 32-bit record count at any L.
-__device__ __forceinline__ void dma_tile(const unsigned short* base, const int* src, int loads,
-                                         int row_bytes, int j0, int L, unsigned char* dst_shared) {
-  LDS_AS unsigned char* dst = (LDS_AS unsigned char*)dst_shared;
-  const __amdgpu_buffer_rsrc_t rsrc =
-      make_rsrc((const unsigned char*)base + (size_t)j0 * row_bytes,
-                (unsigned)min(max(L - j0, 0), kBC) * row_bytes);
-#pragma unroll
-  for (int s = 0; s < loads; ++s)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + s * 1024), 16, src[s], 0,
-                                             0, 0);
 }
 
 template <int D, int HWG, int NB>
@@ -263,7 +194,7 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
   }
   auto load_tile = [&] __device__ (const unsigned short* base, const int (&src)[LOADS], int tile,
                        int lds_off) __attribute__((always_inline)) {
-    dma_tile(base, src, LOADS, ROWB, tile * kBC, Lk, smem + lds_off + wave * LOADS * 1024);
+    dma_tile(base, src, LOADS, ROWB, tile * kBC, Lk, kBC, smem + lds_off + wave * LOADS * 1024);
   };
 
   // ---- per-lane LDS read offsets
@@ -592,11 +523,6 @@ int launch_d(const void* q, const void* k, const void* v, void* out, float* lse,
   }
 }
 
-bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
-  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + bn && y < x + an;
-}
-
 // Argument checks shared by the entry points, then the launch.
 int check_and_launch(const void* q, const void* k, const void* v, void* out, float* lse,
                      const Shape& sh, float scale, int causal, hipStream_t stream) {
@@ -781,8 +707,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
 
   for (int t0 = j_begin + wave * kBC; t0 < j_end; t0 += kDecWaves * kBC) {
     wait_lgkm0();   // the previous tile's LDS reads are done before it is overwritten
-    dma_tile(kbase, k_src, LOADS, ROWB, t0, j_end, wbuf);
-    dma_tile(vbase, v_src, LOADS, ROWB, t0, j_end, wbuf + TILE);
+    dma_tile(kbase, k_src, LOADS, ROWB, t0, j_end, kBC, wbuf);
+    dma_tile(vbase, v_src, LOADS, ROWB, t0, j_end, kBC, wbuf + TILE);
     wait_vmcnt<0>();
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {

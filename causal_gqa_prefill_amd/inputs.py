@@ -41,6 +41,60 @@ def make_qkv(B, L, n_q, n_kv, d_h, seed):
     return tuple(out)
 
 
+def _e4m3_positive_values():
+    """Values of the OCP e4m3 codes 0x00 .. 0x7E (increasing): exponent bits
+    6..3 with bias 7, mantissa bits 2..0, subnormals m * 2^-9."""
+    codes = np.arange(127)
+    e = codes >> 3
+    m = codes & 7
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+
+
+def e4m3_bits(x) -> np.ndarray:
+    """float32 array -> OCP e4m3 codes (uint8), round to nearest, ties to the
+    even code.  |x| must not exceed 464 (the largest finite code's range)."""
+    x = np.asarray(x, dtype=np.float32)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    # float32 holds every e4m3 value, and the two differences below are exact
+    # (neighbouring codes are within a factor 2 of each other, or zero)
+    table = _e4m3_positive_values().astype(np.float32)
+    step = 1 << 22   # bounded temporaries for tensors of hundreds of millions of values
+    for i0 in range(0, flat.size, step):
+        xs = flat[i0:i0 + step]
+        a = np.abs(xs)
+        if np.any(a > 464.0) or not np.all(np.isfinite(a)):
+            raise ValueError("values outside the e4m3 range")
+        hi = np.clip(np.searchsorted(table, a), 1, 126)
+        lo = hi - 1
+        dlo = a - table[lo]
+        dhi = table[hi] - a
+        pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+        code = np.where(pick_hi, hi, lo).astype(np.uint8)
+        code[a >= table[126]] = 126
+        code[np.signbit(xs)] |= np.uint8(0x80)
+        out[i0:i0 + step] = code
+    return out.reshape(x.shape)
+
+
+def make_fp8_qkv(B, Lq, Lk, n_q, n_kv, d_h, seed):
+    """Q [B,n_q,Lq,d_h], K, V [B,n_kv,Lk,d_h] as OCP e4m3 codes with one fp32
+    descale factor each: the same N(0, 1) float32 draws as make_chunk_qkv
+    (order Q, K, V from one stream), each tensor divided by
+    descale = max|x| / 448 and rounded to e4m3 (nearest even).  Returns
+    (q, k, v, descale_q, descale_k, descale_v)."""
+    rng = np.random.default_rng(seed)
+    codes, scales = [], []
+    for heads, length in ((n_q, Lq), (n_kv, Lk), (n_kv, Lk)):
+        x = rng.standard_normal((B, heads, length, d_h), dtype=np.float32)
+        s = np.float32(np.max(np.abs(x)) / np.float32(448.0))
+        np.divide(x, s, out=x)
+        codes.append(e4m3_bits(x))
+        scales.append(float(s))
+        del x
+    return (*codes, *scales)
+
+
 def make_config_qkv(cfg):
     return make_qkv(cfg.B, cfg.L, cfg.n_q, cfg.n_kv, cfg.d_h, cfg.seed)
 

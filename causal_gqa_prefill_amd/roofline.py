@@ -15,6 +15,7 @@ mask the count is 4 * L^2 * d_h * n_q (the FlashAttention-2 convention).
 # MI355X published peaks (AMD datasheet figures, dense, no sparsity)
 MI355X_BF16_DENSE_TFLOPS = 2516.6   # 256 CU * 4096 flop/clk * 2.4 GHz
 MI355X_HBM_GBPS = 8000.0
+MI355X_FP8_DENSE_TFLOPS = 5000.0     # dense fp8 matrix-core peak (datasheet)
 
 
 def attn_flops(B, L, n_q, d_h, causal=True):

@@ -138,6 +138,34 @@ int attn_merge_partials(const void *o_a, const float *lse_a, const void *o_b,
                         int d_h, hipStream_t stream);
 
 /*
+ * FP8 chunked prefill: attn_prefill_fwd_chunk with Q, K and V given as OCP
+ * e4m3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities; S.1111.111 is NaN; largest finite 448) and one fp32 descale
+ * factor per tensor, true value = decoded code x descale.  FP8 matrix-core
+ * products buy throughput on the compute-dense part of prefill ("flops /
+ * prefill-attention", section "Workarounds", FP8 attention).
+ *   q      : device pointer, e4m3 [B, n_q, Lq, d_h]   (one byte per element)
+ *   k, v   : device pointers, e4m3 [B, n_kv, Lk, d_h]
+ *   out    : device pointer, bf16 [B, n_q, Lq, d_h]; lse: fp32 [B, n_q, Lq]
+ *   d_h must be 128; scale, descale_q, descale_k, descale_v finite; the
+ *   other arguments, the causal rule and q_offset as for
+ *   attn_prefill_fwd_chunk.
+ * Numerics: Q K^T in e4m3 x e4m3 with fp32 accumulation (exact products);
+ * the softmax in fp32; the weights P, taken relative to a running reference
+ * max that is never more than 2^8 below the row max seen so far, are rounded
+ * to e4m3 (nearest even: relative error <= 2^-4, and weights below 2^-10 of
+ * the reference round to 0) before P V; the row sum adds the unrounded
+ * weights; O = descale_v x (P V) / sum, rounded once to bf16.
+ * Errors as for attn_prefill_fwd_chunk (ATTN_PREFILL_ERR_BAD_HEADDIM for
+ * d_h != 128, ATTN_PREFILL_ERR_BAD_SCALE also when scale x descale_q x
+ * descale_k overflows fp32).
+ */
+int attn_prefill_fwd_fp8(const void *q, const void *k, const void *v, void *out, float *lse,
+                         int B, int Lq, int Lk, int q_offset, int n_q, int n_kv, int d_h,
+                         float scale, float descale_q, float descale_k, float descale_v,
+                         int causal, hipStream_t stream);
+
+/*
  * Decode: one new query per sequence against the sequence's whole K/V cache.
  * The query is token Lk - 1 of its sequence, its own key and value already in
  * the cache, so it sees every cached key; attention becomes a matrix-vector

@@ -43,6 +43,19 @@ def load_library(path):
         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
         ctypes.POINTER(ctypes.c_uint64), ctypes.c_int,
     ]
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.oracle_attn_rows_chunk_fp8.restype = ctypes.c_int
+    lib.oracle_attn_rows_chunk_fp8.argtypes = [
+        u8p, u8p, u8p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+        ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int,
+        ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+        dp, dp, dp, ctypes.POINTER(ctypes.c_uint64), ctypes.c_int,
+    ]
+    lib.oracle_e4m3_table.restype = None
+    lib.oracle_e4m3_table.argtypes = [dp]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_version.restype = ctypes.c_int
     return lib
@@ -180,3 +193,56 @@ def merge_partials(o_a, lse_a, o_b, lse_b):
     out = (part_a + part_b) / safe_total[:, None]
     lse = np.where(both_empty, -np.inf, m_safe + np.log(safe_total))
     return out, lse
+
+
+def e4m3_table(lib=None):
+    """The oracle's decoded value of every OCP e4m3 code (float64 [256])."""
+    out = np.empty(256, dtype=np.float64)
+    (lib or _load()).oracle_e4m3_table(out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    return out
+
+
+def attention_rows_chunk_fp8(q, k, v, scale, descale_q, descale_k, descale_v, causal=True,
+                             q_offset=0, rows=None, threads=0, lib=None):
+    """Oracle attention of a chunk with OCP e4m3 inputs ("flops /
+    prefill-attention", section "Workarounds", FP8 attention): codes decoded
+    exactly, times their fp32 descale factors, then the plain fp64 attention.
+
+    q: uint8 [B, n_q, Lq, d_h]; k, v: uint8 [B, n_kv, Lk, d_h] (e4m3 codes).
+    Returns (out [n_rows, d_h], lse [n_rows], bound [n_rows, d_h], flops):
+    bound is, per element, 2^-4 sum_j P_j |v_j| + 2^-10 max_j P_j sum_j |v_j|
+    over the visible keys, the most that rounding the weights to e4m3 can
+    move that element of out.
+    """
+    if q.ndim != 4 or k.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B, heads, L, d_h]")
+    B, n_q, Lq, d_h = q.shape
+    n_kv, Lk = k.shape[1], k.shape[2]
+    for name, a, shape in (("q", q, (B, n_q, Lq, d_h)), ("k", k, (B, n_kv, Lk, d_h)),
+                           ("v", v, (B, n_kv, Lk, d_h))):
+        if a.dtype != np.uint8 or a.shape != shape:
+            raise ValueError(f"{name} must be uint8 e4m3 codes of shape {shape}")
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    if rows is None:
+        n_rows = B * n_q * Lq
+        rows_p = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = int(rows.size)
+        rows_p = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    out = np.empty((n_rows, d_h), dtype=np.float64)
+    lse = np.empty((n_rows,), dtype=np.float64)
+    bound = np.empty((n_rows, d_h), dtype=np.float64)
+    flops = ctypes.c_uint64(0)
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = (lib or _load()).oracle_attn_rows_chunk_fp8(
+        q.ctypes.data_as(u8p), k.ctypes.data_as(u8p), v.ctypes.data_as(u8p),
+        B, Lq, Lk, int(q_offset), n_q, n_kv, d_h, float(np.float32(scale)),
+        float(np.float32(descale_q)), float(np.float32(descale_k)),
+        float(np.float32(descale_v)), int(causal), rows_p, n_rows,
+        out.ctypes.data_as(dp), lse.ctypes.data_as(dp), bound.ctypes.data_as(dp),
+        ctypes.byref(flops), int(threads))
+    if rc != OK:
+        raise ValueError(f"oracle_attn_rows_chunk_fp8 failed with code {rc}")
+    return out, lse, bound, int(flops.value)

@@ -34,9 +34,17 @@
  * j <= q_off + i.  With Lq = Lk = L and q_off = 0 this is the whole-sequence
  * case above.
  *
- * Layouts: q [B, n_q, Lq, d_h], k and v [B, n_kv, Lk, d_h], all bf16 bit
- * patterns (uint16), row-major, d_h fastest.  A "row" is the flat index
- * (b * n_q + h) * Lq + i of one query.
+ * FP8 inputs ("flops / prefill-attention", section "Workarounds", FP8
+ * attention): q, k, v may instead be OCP e4m3 codes with an fp32 descale
+ * factor each; the oracle decodes every code exactly (sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, subnormals below 2^-6, S.1111.111 = NaN),
+ * multiplies by the descale in fp64 and runs the same plain attention.  For
+ * that path it also returns, per output element, the bound that rounding
+ * the weights to e4m3 can move it by (see oracle_attn_rows_chunk_fp8).
+ *
+ * Layouts: q [B, n_q, Lq, d_h], k and v [B, n_kv, Lk, d_h], bf16 bit
+ * patterns (uint16) or e4m3 codes (uint8), row-major, d_h fastest.  A "row"
+ * is the flat index (b * n_q + h) * Lq + i of one query.
  *
  * Parity pins: every function here is pinned by CPU tests against brute force
  * in 50-digit arithmetic, closed forms and a library routine; nothing in it is
@@ -54,7 +62,7 @@
 #define ORACLE_BAD_ARG 1
 #define ORACLE_NO_MEMORY 2
 
-int oracle_version(void) { return 2; }
+int oracle_version(void) { return 3; }
 
 /* A bf16 bit pattern is the upper half of an fp32 bit pattern, so widening is
  * exact: shift into place, reinterpret as float, convert to double. */
@@ -66,12 +74,46 @@ static double widen_bf16(uint16_t bits)
     return (double)f;
 }
 
-/* One query row, done the plain way.  s and w are scratch rows of length Lk. */
-static void one_row(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+/* An OCP e4m3 code, decoded from the format's definition: sign bit 7,
+ * exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent 0 holds the
+ * subnormals m * 2^-9; exponent 15 with mantissa 7 is NaN (there is no
+ * infinity).  Exact in double. */
+static double widen_e4m3(uint8_t code)
+{
+    const int sign = code >> 7;
+    const int e = (code >> 3) & 15;
+    const int m = code & 7;
+    double x;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        x = ldexp((double)m, -9);
+    else
+        x = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -x : x;
+}
+
+enum { KIND_BF16 = 0, KIND_E4M3 = 1 };
+
+/* Element idx of a tensor of the given kind, widened exactly, times mul. */
+static inline double elem(int kind, const void *base, int64_t idx, double mul)
+{
+    if (kind == KIND_BF16)
+        return widen_bf16(((const uint16_t *)base)[idx]) * mul;
+    return widen_e4m3(((const uint8_t *)base)[idx]) * mul;
+}
+
+/* One query row, done the plain way.  s and w are scratch rows of length Lk.
+ * dq, dk, dv multiply the decoded q, k, v (1 for bf16).  bound, if not NULL,
+ * receives per output element 2^-4 sum_j P_j |v_j| + 2^-10 max_j P_j
+ * sum_j |v_j| over the visible keys: the most that rounding each weight to
+ * e4m3 (relative error <= 2^-4 in the normal range, absolute <= 2^-10 of
+ * the reference max below it) can move the element. */
+static void one_row(int kind, const void *q, const void *k, const void *v,
                     int64_t Lq, int64_t Lk, int64_t q_off, int64_t n_q,
-                    int64_t n_kv, int64_t d_h, double scale, int causal,
-                    int64_t row, double *s, double *w, double *out,
-                    double *lse, uint64_t *flops)
+                    int64_t n_kv, int64_t d_h, double scale, double dq, double dk,
+                    double dv, int causal, int64_t row, double *s, double *w,
+                    double *out, double *lse, double *bound, uint64_t *flops)
 {
     const int64_t L = Lk;
     const int64_t g = n_q / n_kv;
@@ -79,9 +121,9 @@ static void one_row(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     const int64_t h = (row / Lq) % n_q;
     const int64_t b = row / (Lq * n_q);
     const int64_t kvh = h / g;
-    const uint16_t *qrow = q + ((b * n_q + h) * Lq + i) * d_h;
-    const uint16_t *kbase = k + (b * n_kv + kvh) * Lk * d_h;
-    const uint16_t *vbase = v + (b * n_kv + kvh) * Lk * d_h;
+    const int64_t qrow = ((b * n_q + h) * Lq + i) * d_h;
+    const int64_t kbase = (b * n_kv + kvh) * Lk * d_h;
+    const int64_t vbase = (b * n_kv + kvh) * Lk * d_h;
     /* visible keys: j <= q_off + i when causal, all Lk keys otherwise */
     const int64_t n_vis = causal ? q_off + i + 1 : Lk;
 
@@ -89,10 +131,10 @@ static void one_row(const uint16_t *q, const uint16_t *k, const uint16_t *v,
      *    dot products are never formed */
     for (int64_t j = 0; j < L; ++j) {
         if (j < n_vis) {
-            const uint16_t *krow = kbase + j * d_h;
+            const int64_t krow = kbase + j * d_h;
             double dot = 0.0;
             for (int64_t t = 0; t < d_h; ++t)
-                dot += widen_bf16(qrow[t]) * widen_bf16(krow[t]);
+                dot += elem(kind, q, qrow + t, dq) * elem(kind, k, krow + t, dk);
             s[j] = scale * dot;
         } else {
             s[j] = -INFINITY;
@@ -115,10 +157,25 @@ static void one_row(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     for (int64_t t = 0; t < d_h; ++t)
         out[t] = 0.0;
     for (int64_t j = 0; j < n_vis; ++j) {
-        const uint16_t *vrow = vbase + j * d_h;
+        const int64_t vrow = vbase + j * d_h;
         const double p = w[j];
         for (int64_t t = 0; t < d_h; ++t)
-            out[t] += p * widen_bf16(vrow[t]);
+            out[t] += p * elem(kind, v, vrow + t, dv);
+    }
+    /* 5b. the e4m3 weight-rounding bound per element */
+    if (bound) {
+        double p_max = 0.0;
+        for (int64_t j = 0; j < n_vis; ++j)
+            if (w[j] > p_max) p_max = w[j];
+        for (int64_t t = 0; t < d_h; ++t) {
+            double weighted = 0.0, plain = 0.0;
+            for (int64_t j = 0; j < n_vis; ++j) {
+                const double a = fabs(elem(kind, v, vbase + j * d_h + t, dv));
+                weighted += w[j] * a;
+                plain += a;
+            }
+            bound[t] = ldexp(weighted, -4) + ldexp(p_max * plain, -10);
+        }
     }
     /* 6. saved row statistic: natural-log log-sum-exp of the scaled scores */
     *lse = m + log(total);
@@ -135,11 +192,13 @@ static void one_row(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  *   threads <= 0 leaves the OpenMP default.
  * Returns ORACLE_OK, ORACLE_BAD_ARG or ORACLE_NO_MEMORY.
  */
-int oracle_attn_rows_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                           int64_t B, int64_t Lq, int64_t Lk, int64_t q_off,
-                           int64_t n_q, int64_t n_kv, int64_t d_h, float scale,
-                           int causal, const int64_t *rows, int64_t n_rows,
-                           double *out, double *lse, uint64_t *flops, int threads)
+static int rows_generic(int kind, const void *q, const void *k, const void *v,
+                        int64_t B, int64_t Lq, int64_t Lk, int64_t q_off,
+                        int64_t n_q, int64_t n_kv, int64_t d_h, float scale,
+                        double dq, double dk, double dv,
+                        int causal, const int64_t *rows, int64_t n_rows,
+                        double *out, double *lse, double *bound, uint64_t *flops,
+                        int threads)
 {
     if (!q || !k || !v || !out || !lse || !flops) return ORACLE_BAD_ARG;
     if (B < 1 || Lq < 1 || Lk < 1 || n_q < 1 || n_kv < 1 || d_h < 1) return ORACLE_BAD_ARG;
@@ -174,14 +233,54 @@ int oracle_attn_rows_chunk(const uint16_t *q, const uint16_t *k, const uint16_t 
                 continue;
             }
             const int64_t row = rows ? rows[r] : r;
-            one_row(q, k, v, Lq, Lk, q_off, n_q, n_kv, d_h, sc, causal, row, s, w,
-                    out + r * d_h, lse + r, &count);
+            one_row(kind, q, k, v, Lq, Lk, q_off, n_q, n_kv, d_h, sc, dq, dk, dv, causal,
+                    row, s, w, out + r * d_h, lse + r, bound ? bound + r * d_h : NULL,
+                    &count);
         }
         free(s);
         free(w);
     }
     *flops = count;
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+int oracle_attn_rows_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           int64_t B, int64_t Lq, int64_t Lk, int64_t q_off,
+                           int64_t n_q, int64_t n_kv, int64_t d_h, float scale,
+                           int causal, const int64_t *rows, int64_t n_rows,
+                           double *out, double *lse, uint64_t *flops, int threads)
+{
+    return rows_generic(KIND_BF16, q, k, v, B, Lq, Lk, q_off, n_q, n_kv, d_h, scale,
+                        1.0, 1.0, 1.0, causal, rows, n_rows, out, lse, NULL, flops, threads);
+}
+
+/*
+ * The chunk with e4m3 inputs: q, k, v are OCP e4m3 codes, decoded exactly
+ * and multiplied by descale_q, descale_k, descale_v (fp32 values, widened
+ * exactly).  Arguments and results otherwise as oracle_attn_rows_chunk;
+ * bound (NULL or [n_rows, d_h]) receives the per-element weight-rounding
+ * bound described at one_row.
+ */
+int oracle_attn_rows_chunk_fp8(const uint8_t *q, const uint8_t *k, const uint8_t *v,
+                               int64_t B, int64_t Lq, int64_t Lk, int64_t q_off,
+                               int64_t n_q, int64_t n_kv, int64_t d_h, float scale,
+                               float descale_q, float descale_k, float descale_v,
+                               int causal, const int64_t *rows, int64_t n_rows,
+                               double *out, double *lse, double *bound, uint64_t *flops,
+                               int threads)
+{
+    if (!isfinite(descale_q) || !isfinite(descale_k) || !isfinite(descale_v))
+        return ORACLE_BAD_ARG;
+    return rows_generic(KIND_E4M3, q, k, v, B, Lq, Lk, q_off, n_q, n_kv, d_h, scale,
+                        (double)descale_q, (double)descale_k, (double)descale_v, causal,
+                        rows, n_rows, out, lse, bound, flops, threads);
+}
+
+/* Decoded value of every e4m3 code (for pinning the decoder): out[256]. */
+void oracle_e4m3_table(double *out)
+{
+    for (int c = 0; c < 256; ++c)
+        out[c] = widen_e4m3((uint8_t)c);
 }
 
 /* Whole-sequence attention for the requested rows: the chunk with

@@ -23,8 +23,8 @@ def test_library_exports_header_symbols():
     lib = binding.library()
     names = _declared_functions()
     assert names == ["attn_decode_fwd", "attn_decode_workspace_bytes", "attn_merge_partials",
-                     "attn_prefill_fwd", "attn_prefill_fwd_chunk", "attn_prefill_strerror",
-                     "attn_prefill_version"]
+                     "attn_prefill_fwd", "attn_prefill_fwd_chunk", "attn_prefill_fwd_fp8",
+                     "attn_prefill_strerror", "attn_prefill_version"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -167,3 +167,27 @@ def _call_decode(**kw):
 ])
 def test_decode_bad_arguments_rejected_on_host(kw, code):
     assert _call_decode(**kw) == code
+
+
+def _call_fp8(**kw):
+    args = dict(q=ALIGNED, k=ALIGNED + 0x10000000, v=ALIGNED + 0x20000000,
+                out=ALIGNED + 0x30000000, lse=ALIGNED + 0x40000000,
+                B=1, Lq=64, Lk=128, q_offset=64, n_q=4, n_kv=2, d_h=128, scale=0.088,
+                dq=0.01, dk=0.01, dv=0.01, causal=1, stream=0)
+    args.update(kw)
+    return binding.fwd_fp8_raw(args["q"], args["k"], args["v"], args["out"], args["lse"],
+                               args["B"], args["Lq"], args["Lk"], args["q_offset"], args["n_q"],
+                               args["n_kv"], args["d_h"], args["scale"], args["dq"], args["dk"],
+                               args["dv"], args["causal"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v=0), 1), (dict(B=0), 2), (dict(Lk=0), 2), (dict(n_q=3), 3),
+    (dict(d_h=64), 4), (dict(dq=float("nan")), 5), (dict(dv=float("inf")), 5),
+    (dict(scale=1e30, dq=1e30, dk=1e30), 5), (dict(causal=2), 6),
+    (dict(q_offset=65), 11), (dict(q_offset=-3, causal=0), 11),
+    (dict(k=ALIGNED + 0x10000008), 7),
+    (dict(out=ALIGNED + 0x10000000 + 4096), 9), (dict(lse=ALIGNED), 9),
+])
+def test_fp8_bad_arguments_rejected_on_host(kw, code):
+    assert _call_fp8(**kw) == code

@@ -25,15 +25,22 @@ MUTANTS = {
     "mask one too wide": ("causal ? q_off + i + 1 : Lk",
                           "causal ? (q_off + i + 2 < Lk ? q_off + i + 2 : Lk) : Lk"),
     "chunk offset ignored": ("causal ? q_off + i + 1 : Lk", "causal ? i + 1 : Lk"),
-    "kv heads strided by Lq": ("const uint16_t *kbase = k + (b * n_kv + kvh) * Lk * d_h;",
-                               "const uint16_t *kbase = k + (b * n_kv + kvh) * Lq * d_h;"),
+    "kv heads strided by Lq": ("const int64_t kbase = (b * n_kv + kvh) * Lk * d_h;",
+                               "const int64_t kbase = (b * n_kv + kvh) * Lq * d_h;"),
+    "e4m3 bias 8": ("x = ldexp(1.0 + m / 8.0, e - 7);", "x = ldexp(1.0 + m / 8.0, e - 8);"),
+    "e4m3 subnormals as normals": ("x = ldexp((double)m, -9);", "x = ldexp(1.0 + m / 8.0, -6);"),
+    "descale ignored": ("return widen_e4m3(((const uint8_t *)base)[idx]) * mul;",
+                        "return widen_e4m3(((const uint8_t *)base)[idx]); (void)mul;"),
+    "bound without weights": ("weighted += w[j] * a;", "weighted += a / n_vis;"),
     "kv head h mod n_kv": ("const int64_t kvh = h / g;", "const int64_t kvh = h % n_kv;"),
     "log2 in lse": ("*lse = m + log(total);", "*lse = m + log2(total);"),
-    "K read transposed": ("dot += widen_bf16(qrow[t]) * widen_bf16(krow[t]);",
-                          "dot += widen_bf16(qrow[t]) * widen_bf16(kbase[t * L + j]); (void)krow;"),
+    "K read transposed": ("dot += elem(kind, q, qrow + t, dq) * elem(kind, k, krow + t, dk);",
+                          "dot += elem(kind, q, qrow + t, dq) * elem(kind, k, kbase + t * L + j, dk);"
+                          " (void)krow;"),
     "scale ignored": ("s[j] = scale * dot;", "s[j] = dot / sqrt((double)d_h); (void)scale;"),
     "weights not normalised": ("w[j] = w[j] / total;", "w[j] = w[j];"),
-    "V read from K": ("const uint16_t *vbase = v +", "const uint16_t *vbase = k +"),
+    "V read from K": ("out[t] += p * elem(kind, v, vrow + t, dv);",
+                      "out[t] += p * elem(kind, k, vrow + t, dv);"),
     "lse without max": ("*lse = m + log(total);", "*lse = log(total);"),
     "flops halved": ("(uint64_t)(4 * d_h * n_vis)", "(uint64_t)(2 * d_h * n_vis)"),
 }
@@ -98,8 +105,45 @@ def _check_chunk_brute(lib):
                 np.max(np.abs(l - ref_l.reshape(-1))) <= 1e-14)
 
 
+def _check_fp8(lib):
+    # the e4m3 decoder against torch, the fp8 path against the bf16 path on
+    # values both hold exactly (power-of-two descales), and the rounding
+    # bound against a direct simulation
+    torch = pytest.importorskip("torch")
+    tab = oracle.e4m3_table(lib=lib)
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    if not np.all((np.isnan(tab) & np.isnan(ref)) | (tab == ref)):
+        return False
+    q, k, v, *_ = inputs.make_fp8_qkv(1, 6, 20, 2, 1, 8, 86)
+    dq, dk, dv = 0.25, 0.5, 2.0
+    to_b = lambda c, s_: inputs.bf16_bits((ref[c] * s_).astype(np.float32))
+    o8, l8, bnd, _ = oracle.attention_rows_chunk_fp8(q, k, v, 0.7, dq, dk, dv, True, 14, lib=lib)
+    ob, lb, _ = oracle.attention_rows_chunk(to_b(q, dq), to_b(k, dk), to_b(v, dv), 0.7, True,
+                                            q_offset=14, lib=lib)
+    if not (np.max(np.abs(o8 - ob)) <= 1e-15 and np.max(np.abs(l8 - lb)) <= 1e-15):
+        return False
+    vv = ref[v][0, 0] * dv
+    qv, kv_ = ref[q][0] * dq, ref[k][0, 0] * dk
+    for h in range(2):
+        for i in range(6):
+            r = h * 6 + i
+            sc = kv_[:15 + i] @ qv[h, i] * float(np.float32(0.7)) / math.log(2)
+            p = np.exp2(sc - sc.max())
+            p_hat = ref[inputs.e4m3_bits(p.astype(np.float32))]
+            err = np.abs((p_hat @ vv[:15 + i]) / p.sum() - o8[r])
+            if np.any(err > bnd[r] * (1 + 1e-9) + 1e-12):
+                return False
+            # and it is the stated expression, not merely some valid bound
+            P = p / p.sum()
+            a = np.abs(vv[:15 + i])
+            want = 2.0 ** -4 * (P @ a) + 2.0 ** -10 * P.max() * a.sum(axis=0)
+            if np.max(np.abs(bnd[r] - want)) > 1e-12 * max(1.0, np.max(want)):
+                return False
+    return True
+
+
 CHECKS = [_check_brute, _check_large_scores, _check_constant_v,
-          _check_zero_query, _check_flops, _check_chunk_brute]
+          _check_zero_query, _check_flops, _check_chunk_brute, _check_fp8]
 
 
 def _build_variant(tmp_path, name, src):
