@@ -56,6 +56,21 @@ def load_library(path):
     ]
     lib.oracle_e4m3_table.restype = None
     lib.oracle_e4m3_table.argtypes = [dp]
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.oracle_attn_bwd_rowstats.restype = ctypes.c_int
+    lib.oracle_attn_bwd_rowstats.argtypes = [
+        u16p, u16p, u16p, u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, ctypes.c_int]
+    lib.oracle_attn_bwd_dq.restype = ctypes.c_int
+    lib.oracle_attn_bwd_dq.argtypes = [
+        u16p, u16p, u16p, u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, i64p,
+        ctypes.c_int64, dp, ctypes.c_int]
+    lib.oracle_attn_bwd_dkdv.restype = ctypes.c_int
+    lib.oracle_attn_bwd_dkdv.argtypes = [
+        u16p, u16p, u16p, u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, i64p,
+        ctypes.c_int64, dp, dp, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_version.restype = ctypes.c_int
     return lib
@@ -246,3 +261,93 @@ def attention_rows_chunk_fp8(q, k, v, scale, descale_q, descale_k, descale_v, ca
     if rc != OK:
         raise ValueError(f"oracle_attn_rows_chunk_fp8 failed with code {rc}")
     return out, lse, bound, int(flops.value)
+
+
+# ---------------------------------------------------------------------------
+# backward pass ("Long-Context Attention Explained", section "What
+# FlashAttention does not change": gradients recomputed from the saved row
+# statistics); whole sequences, bf16 inputs as uint16 bits
+# ---------------------------------------------------------------------------
+def _bwd_shapes(q, k, v, dout):
+    if q.ndim != 4 or k.ndim != 4:
+        raise ValueError("q, k, v, dout must be 4-D [B, heads, L, d_h]")
+    B, n_q, L, d = q.shape
+    n_kv = k.shape[1]
+    q = _bits(q, (B, n_q, L, d), "q")
+    k = _bits(k, (B, n_kv, L, d), "k")
+    v = _bits(v, (B, n_kv, L, d), "v")
+    dout = _bits(dout, (B, n_q, L, d), "dout")
+    if n_q % n_kv:
+        raise ValueError("n_q must be a multiple of n_kv")
+    return q, k, v, dout, B, n_q, n_kv, L, d
+
+
+def attention_bwd_rowstats(q, k, v, dout, scale, causal=True, threads=0, lib=None):
+    """Every row's LSE and delta = dO . O (exact O), fp64 [B * n_q * L] each."""
+    q, k, v, dout, B, n_q, n_kv, L, d = _bwd_shapes(q, k, v, dout)
+    lse = np.empty(B * n_q * L)
+    delta = np.empty(B * n_q * L)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = (lib or _load()).oracle_attn_bwd_rowstats(
+        q.ctypes.data_as(u16p), k.ctypes.data_as(u16p), v.ctypes.data_as(u16p),
+        dout.ctypes.data_as(u16p), B, L, n_q, n_kv, d, float(np.float32(scale)), int(causal),
+        lse.ctypes.data_as(dp), delta.ctypes.data_as(dp), int(threads))
+    if rc != OK:
+        raise ValueError(f"oracle_attn_bwd_rowstats failed with code {rc}")
+    return lse, delta
+
+
+def attention_bwd_dq(q, k, v, dout, scale, causal, lse, delta, rows, threads=0, lib=None):
+    """dQ [len(rows), d_h] for flat query rows (b * n_q + h) * L + i."""
+    q, k, v, dout, B, n_q, n_kv, L, d = _bwd_shapes(q, k, v, dout)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    lse = np.ascontiguousarray(lse, dtype=np.float64)
+    delta = np.ascontiguousarray(delta, dtype=np.float64)
+    out = np.empty((rows.size, d))
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = (lib or _load()).oracle_attn_bwd_dq(
+        q.ctypes.data_as(u16p), k.ctypes.data_as(u16p), v.ctypes.data_as(u16p),
+        dout.ctypes.data_as(u16p), B, L, n_q, n_kv, d, float(np.float32(scale)), int(causal),
+        lse.ctypes.data_as(dp), delta.ctypes.data_as(dp),
+        rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size,
+        out.ctypes.data_as(dp), int(threads))
+    if rc != OK:
+        raise ValueError(f"oracle_attn_bwd_dq failed with code {rc}")
+    return out
+
+
+def attention_bwd_dkdv(q, k, v, dout, scale, causal, lse, delta, rows, threads=0, lib=None):
+    """(dK, dV) [len(rows), d_h] for flat key rows (b * n_kv + kvh) * L + j."""
+    q, k, v, dout, B, n_q, n_kv, L, d = _bwd_shapes(q, k, v, dout)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    lse = np.ascontiguousarray(lse, dtype=np.float64)
+    delta = np.ascontiguousarray(delta, dtype=np.float64)
+    dk = np.empty((rows.size, d))
+    dv = np.empty((rows.size, d))
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = (lib or _load()).oracle_attn_bwd_dkdv(
+        q.ctypes.data_as(u16p), k.ctypes.data_as(u16p), v.ctypes.data_as(u16p),
+        dout.ctypes.data_as(u16p), B, L, n_q, n_kv, d, float(np.float32(scale)), int(causal),
+        lse.ctypes.data_as(dp), delta.ctypes.data_as(dp),
+        rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size,
+        dk.ctypes.data_as(dp), dv.ctypes.data_as(dp), int(threads))
+    if rc != OK:
+        raise ValueError(f"oracle_attn_bwd_dkdv failed with code {rc}")
+    return dk, dv
+
+
+def attention_bwd(q, k, v, dout, scale, causal=True, threads=0, lib=None):
+    """Every row of dQ [B, n_q, L, d_h], dK and dV [B, n_kv, L, d_h] (fp64),
+    plus the row statistics (lse, delta)."""
+    B, n_q, L, d = q.shape
+    n_kv = k.shape[1]
+    lse, delta = attention_bwd_rowstats(q, k, v, dout, scale, causal, threads, lib)
+    dq = attention_bwd_dq(q, k, v, dout, scale, causal, lse, delta,
+                          np.arange(B * n_q * L), threads, lib)
+    dk, dv = attention_bwd_dkdv(q, k, v, dout, scale, causal, lse, delta,
+                                np.arange(B * n_kv * L), threads, lib)
+    return (dq.reshape(B, n_q, L, d), dk.reshape(B, n_kv, L, d), dv.reshape(B, n_kv, L, d),
+            lse, delta)

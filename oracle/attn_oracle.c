@@ -295,6 +295,160 @@ int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                   rows, n_rows, out, lse, flops, threads);
 }
 
+/* ------------------------------------------------------------------------
+ * Backward pass: the gradients of the attention output with respect to Q, K
+ * and V for an upstream gradient dO, recomputed from the saved row
+ * statistic ("Long-Context Attention Explained", section "What
+ * FlashAttention does not change": the backward pass needs the small saved
+ * row statistics, not the score matrix).  Written out from the definition
+ * O_i = sum_j P_ij v_j, P_ij = exp(s_ij - LSE_i), s_ij = scale q_i . k_j:
+ *     dV_j  = sum_i P_ij dO_i                      (over the query heads of
+ *     dP_ij = dO_i . v_j                             the group and the rows
+ *     D_i   = sum_j P_ij dP_ij  (= dO_i . O_i)        that see key j)
+ *     dS_ij = P_ij (dP_ij - D_i)
+ *     dQ_i  = scale sum_j dS_ij k_j
+ *     dK_j  = scale sum_i dS_ij q_i
+ * Whole sequences only (Lq = Lk = L, query i sees j <= i when causal).
+ * ------------------------------------------------------------------------ */
+
+/* Per-row statistics for the backward pass: lse[r] (natural log, as the
+ * forward oracle) and delta[r] = sum_t dO[r,t] O[r,t] with O the exact
+ * output, for every row r, in fp64. */
+int oracle_attn_bwd_rowstats(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const uint16_t *dout, int64_t B, int64_t L, int64_t n_q,
+                             int64_t n_kv, int64_t d_h, float scale, int causal,
+                             double *lse, double *delta, int threads)
+{
+    if (!dout || !delta) return ORACLE_BAD_ARG;
+    const int64_t n_rows = B * n_q * L;
+    double *o = (double *)malloc((size_t)n_rows * (size_t)d_h * sizeof(double));
+    if (!o) return ORACLE_NO_MEMORY;
+    uint64_t flops = 0;
+    int rc = rows_generic(KIND_BF16, q, k, v, B, L, L, 0, n_q, n_kv, d_h, scale, 1.0, 1.0, 1.0,
+                          causal, NULL, n_rows, o, lse, NULL, &flops, threads);
+    if (rc == ORACLE_OK) {
+        for (int64_t r = 0; r < n_rows; ++r) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < d_h; ++t)
+                acc += widen_bf16(dout[r * d_h + t]) * o[r * d_h + t];
+            delta[r] = acc;
+        }
+    }
+    free(o);
+    return rc;
+}
+
+/* Weight P_ij of query row (b, h, i) on key j of its kv head, from the
+ * exact row statistic lse_i; 0 for a masked key. */
+static double bwd_weight(const uint16_t *q, const uint16_t *k, int64_t L, int64_t n_q,
+                         int64_t n_kv, int64_t d_h, double scale, int causal, int64_t b,
+                         int64_t h, int64_t i, int64_t j, double lse_i)
+{
+    if (causal && j > i) return 0.0;
+    const int64_t kvh = h / (n_q / n_kv);
+    const uint16_t *qrow = q + ((b * n_q + h) * L + i) * d_h;
+    const uint16_t *krow = k + ((b * n_kv + kvh) * L + j) * d_h;
+    double dot = 0.0;
+    for (int64_t t = 0; t < d_h; ++t)
+        dot += widen_bf16(qrow[t]) * widen_bf16(krow[t]);
+    return exp(scale * dot - lse_i);
+}
+
+/* dP_ij = dO_i . v_j */
+static double bwd_dp(const uint16_t *v, const uint16_t *dout, int64_t L, int64_t n_q,
+                     int64_t n_kv, int64_t d_h, int64_t b, int64_t h, int64_t i, int64_t j)
+{
+    const int64_t kvh = h / (n_q / n_kv);
+    const uint16_t *drow = dout + ((b * n_q + h) * L + i) * d_h;
+    const uint16_t *vrow = v + ((b * n_kv + kvh) * L + j) * d_h;
+    double acc = 0.0;
+    for (int64_t t = 0; t < d_h; ++t)
+        acc += widen_bf16(drow[t]) * widen_bf16(vrow[t]);
+    return acc;
+}
+
+/* dQ for the requested query rows (flat (b * n_q + h) * L + i):
+ * dq [n_rows, d_h] fp64.  lse and delta: every row's statistics, from
+ * oracle_attn_bwd_rowstats. */
+int oracle_attn_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       const uint16_t *dout, int64_t B, int64_t L, int64_t n_q, int64_t n_kv,
+                       int64_t d_h, float scale, int causal, const double *lse,
+                       const double *delta, const int64_t *rows, int64_t n_rows, double *dq,
+                       int threads)
+{
+    if (!q || !k || !v || !dout || !lse || !delta || !rows || !dq) return ORACLE_BAD_ARG;
+    if (B < 1 || L < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || n_q % n_kv) return ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= B * n_q * L) return ORACLE_BAD_ARG;
+    const double sc = (double)scale;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t row = rows[r];
+        const int64_t i = row % L, h = (row / L) % n_q, b = row / (L * n_q);
+        const int64_t kvh = h / (n_q / n_kv);
+        double *out = dq + r * d_h;
+        for (int64_t t = 0; t < d_h; ++t) out[t] = 0.0;
+        const int64_t n_vis = causal ? i + 1 : L;
+        for (int64_t j = 0; j < n_vis; ++j) {
+            const double p = bwd_weight(q, k, L, n_q, n_kv, d_h, sc, causal, b, h, i, j, lse[row]);
+            const double ds = p * (bwd_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j) - delta[row]);
+            const uint16_t *krow = k + ((b * n_kv + kvh) * L + j) * d_h;
+            for (int64_t t = 0; t < d_h; ++t) out[t] += sc * ds * widen_bf16(krow[t]);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* dK and dV for the requested key rows (flat (b * n_kv + kvh) * L + j):
+ * dk, dv [n_rows, d_h] fp64, summed over the g query heads of the group and
+ * every query row that sees key j. */
+int oracle_attn_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         const uint16_t *dout, int64_t B, int64_t L, int64_t n_q, int64_t n_kv,
+                         int64_t d_h, float scale, int causal, const double *lse,
+                         const double *delta, const int64_t *rows, int64_t n_rows, double *dk,
+                         double *dv, int threads)
+{
+    if (!q || !k || !v || !dout || !lse || !delta || !rows || !dk || !dv) return ORACLE_BAD_ARG;
+    if (B < 1 || L < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || n_q % n_kv) return ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= B * n_kv * L) return ORACLE_BAD_ARG;
+    const double sc = (double)scale;
+    const int64_t g = n_q / n_kv;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t row = rows[r];
+        const int64_t j = row % L, kvh = (row / L) % n_kv, b = row / (L * n_kv);
+        double *ok = dk + r * d_h, *ov = dv + r * d_h;
+        for (int64_t t = 0; t < d_h; ++t) ok[t] = ov[t] = 0.0;
+        for (int64_t h = kvh * g; h < kvh * g + g; ++h) {
+            for (int64_t i = causal ? j : 0; i < L; ++i) {
+                const int64_t qrow_id = (b * n_q + h) * L + i;
+                const double p = bwd_weight(q, k, L, n_q, n_kv, d_h, sc, causal, b, h, i, j,
+                                            lse[qrow_id]);
+                const double ds =
+                    p * (bwd_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j) - delta[qrow_id]);
+                const uint16_t *qrow = q + qrow_id * d_h;
+                const uint16_t *drow = dout + qrow_id * d_h;
+                for (int64_t t = 0; t < d_h; ++t) {
+                    ov[t] += p * widen_bf16(drow[t]);
+                    ok[t] += sc * ds * widen_bf16(qrow[t]);
+                }
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* Number of OpenMP threads a parallel region would use (for reporting). */
 int oracle_max_threads(void)
 {

@@ -1,0 +1,134 @@
+"""Pins for the backward-pass functions of the fp64 oracle (no GPU needed).
+
+The gradients of O with respect to Q, K, V for an upstream gradient dO
+("Long-Context Attention Explained", section "What FlashAttention does not
+change": recomputed from the saved row statistics).  Pinned against: torch
+autograd through SDPA in fp64 on the CPU (a library routine), 50-digit
+central differences of an independent brute-force forward pass, and the
+invariants the definition fixes (key gradients of a row sum to zero, value
+gradients sum to the upstream gradients, zero dO gives zero gradients, GQA
+equals MHA with repeated K/V and summed gradients).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from causal_gqa_prefill_amd import inputs
+
+from test_oracle import _vals
+
+
+def _case(B, L, n_q, n_kv, d, seed):
+    q, k, v = inputs.make_qkv(B, L, n_q, n_kv, d, seed)
+    dout = inputs.make_qkv(B, L, n_q, n_kv, d, seed + 500)[0]
+    return q, k, v, dout
+
+
+@pytest.mark.parametrize("B,L,n_q,n_kv,d,causal,scale", [
+    (2, 37, 6, 2, 16, 1, 0.3), (1, 40, 4, 4, 32, 0, 0.2), (1, 65, 8, 1, 8, 1, 0.9),
+    (2, 1, 2, 1, 16, 1, 0.5)])
+def test_bwd_matches_torch_autograd_fp64(B, L, n_q, n_kv, d, causal, scale):
+    torch = pytest.importorskip("torch")
+    q, k, v, do = _case(B, L, n_q, n_kv, d, seed=100 + L)
+    dq, dk, dv, lse, delta = oracle.attention_bwd(q, k, v, do, scale, causal)
+    t = lambda x: torch.from_numpy(_vals(x)).requires_grad_(True)
+    tq, tk, tv = t(q), t(k), t(v)
+    g = n_q // n_kv
+    sc = float(np.float32(scale))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(g, 1), tv.repeat_interleave(g, 1), is_causal=bool(causal), scale=sc)
+    o.backward(torch.from_numpy(_vals(do)))
+    assert np.max(np.abs(dq - tq.grad.numpy())) <= 1e-12
+    assert np.max(np.abs(dk - tk.grad.numpy())) <= 1e-12
+    assert np.max(np.abs(dv - tv.grad.numpy())) <= 1e-12
+    # the row statistics: LSE as the forward oracle, delta = dO . O
+    of, lf, _ = oracle.attention_rows(q, k, v, scale, causal)
+    assert np.array_equal(lse, lf)
+    assert np.max(np.abs(delta - np.sum(_vals(do).reshape(-1, d) * of, axis=1))) <= 1e-13
+
+
+def _mp_forward_loss(mp, qv, kv_, vv, dov, scale, causal):
+    """sum over rows of dO . O in mp arithmetic (an independent forward)."""
+    B, n_q, L, d = len(qv), len(qv[0]), len(qv[0][0]), len(qv[0][0][0])
+    g = n_q // len(kv_[0])
+    total = mp.mpf(0)
+    for b in range(B):
+        for h in range(n_q):
+            for i in range(L):
+                keys = range(i + 1) if causal else range(L)
+                s = [scale * mp.fsum(qv[b][h][i][t] * kv_[b][h // g][j][t] for t in range(d))
+                     for j in keys]
+                z = mp.fsum(mp.e ** x for x in s)
+                for t in range(d):
+                    o = mp.fsum(mp.e ** x * vv[b][h // g][j][t] for x, j in zip(s, keys)) / z
+                    total += dov[b][h][i][t] * o
+    return total
+
+
+def test_bwd_central_differences_50_digits():
+    mpmath = pytest.importorskip("mpmath")
+    mp = mpmath.mp
+    mp.dps = 50
+    B, L, n_q, n_kv, d, causal, scale = 1, 4, 2, 1, 3, 1, 0.7
+    q, k, v, do = _case(B, L, n_q, n_kv, d, seed=7)
+    dq, dk, dv, _, _ = oracle.attention_bwd(q, k, v, do, scale, causal)
+    sc = mp.mpf(float(np.float32(scale)))
+    to_mp = lambda x: [[[[mp.mpf(float(e)) for e in row] for row in hh] for hh in bb]
+                       for bb in _vals(x)]
+    Q, K, V, DO = to_mp(q), to_mp(k), to_mp(v), to_mp(do)
+    eps = mp.mpf(10) ** -20
+    for name, T, grad in (("q", Q, dq), ("k", K, dk), ("v", V, dv)):
+        for idx in [(0, 0, 0, 0), (0, 0, L - 1, d - 1), (0, 1 if T is Q else 0, 2, 1)]:
+            b_, h_, i_, t_ = idx
+            x0 = T[b_][h_][i_][t_]
+            T[b_][h_][i_][t_] = x0 + eps
+            up = _mp_forward_loss(mp, Q, K, V, DO, sc, causal)
+            T[b_][h_][i_][t_] = x0 - eps
+            dn = _mp_forward_loss(mp, Q, K, V, DO, sc, causal)
+            T[b_][h_][i_][t_] = x0
+            fd = float((up - dn) / (2 * eps))
+            assert abs(grad[idx] - fd) <= 1e-13 * max(1.0, abs(fd)), (name, idx, grad[idx], fd)
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_bwd_invariants(causal):
+    B, L, n_q, n_kv, d = 2, 50, 6, 3, 16
+    q, k, v, do = _case(B, L, n_q, n_kv, d, seed=9)
+    dq, dk, dv, _, _ = oracle.attention_bwd(q, k, v, do, 0.25, causal)
+    # sum_j dS_ij = 0 for every row, so the key gradients of a kv head sum to 0
+    assert np.max(np.abs(dk.sum(axis=2))) <= 1e-12
+    # sum_j P_ij = 1, so the value gradients sum to the group's upstream gradients
+    g = n_q // n_kv
+    want = _vals(do).reshape(B, n_kv, g, L, d).sum(axis=(2, 3))
+    assert np.max(np.abs(dv.sum(axis=2) - want)) <= 1e-11
+    # zero upstream gradient: zero gradients
+    z = np.zeros_like(do)
+    dq0, dk0, dv0, _, _ = oracle.attention_bwd(q, k, v, z, 0.25, causal)
+    assert not np.any(dq0) and not np.any(dk0) and not np.any(dv0)
+
+
+def test_bwd_gqa_equals_mha_with_repeated_kv():
+    B, L, n_q, n_kv, d = 1, 33, 8, 2, 16
+    g = n_q // n_kv
+    q, k, v, do = _case(B, L, n_q, n_kv, d, seed=10)
+    dq, dk, dv, _, _ = oracle.attention_bwd(q, k, v, do, 0.3, 1)
+    kr, vr = (np.ascontiguousarray(np.repeat(x, g, axis=1)) for x in (k, v))
+    dqm, dkm, dvm, _, _ = oracle.attention_bwd(q, kr, vr, do, 0.3, 1)
+    assert np.array_equal(dq, dqm)
+    assert np.max(np.abs(dk - dkm.reshape(B, n_kv, g, L, d).sum(axis=2))) <= 1e-13
+    assert np.max(np.abs(dv - dvm.reshape(B, n_kv, g, L, d).sum(axis=2))) <= 1e-13
+
+
+def test_bwd_selected_rows_match_full():
+    B, L, n_q, n_kv, d = 1, 70, 4, 2, 16
+    q, k, v, do = _case(B, L, n_q, n_kv, d, seed=11)
+    dq, dk, dv, lse, delta = oracle.attention_bwd(q, k, v, do, 0.3, 1)
+    rows = np.array([0, 5, 69, 70, 139, 279])
+    assert np.array_equal(oracle.attention_bwd_dq(q, k, v, do, 0.3, 1, lse, delta, rows),
+                          dq.reshape(-1, d)[rows])
+    krows = np.array([0, 1, 69, 70, 139])
+    dks, dvs = oracle.attention_bwd_dkdv(q, k, v, do, 0.3, 1, lse, delta, krows)
+    assert np.array_equal(dks, dk.reshape(-1, d)[krows])
+    assert np.array_equal(dvs, dv.reshape(-1, d)[krows])
+    with pytest.raises(ValueError):
+        oracle.attention_bwd_dq(q, k, v, do, 0.3, 1, lse, delta, np.array([280]))

@@ -32,6 +32,17 @@ MUTANTS = {
     "descale ignored": ("return widen_e4m3(((const uint8_t *)base)[idx]) * mul;",
                         "return widen_e4m3(((const uint8_t *)base)[idx]); (void)mul;"),
     "bound without weights": ("weighted += w[j] * a;", "weighted += a / n_vis;"),
+    "dS sign in dQ": ("p * (bwd_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j) - delta[row])",
+                      "p * (delta[row] - bwd_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j))"),
+    "delta not subtracted in dK": ("p * (bwd_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j) - delta[qrow_id])",
+                                   "p * bwd_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j); (void)delta"),
+    "dQ without scale": ("out[t] += sc * ds * widen_bf16(krow[t]);",
+                         "out[t] += ds * widen_bf16(krow[t]);"),
+    "dV from dS": ("ov[t] += p * widen_bf16(drow[t]);", "ov[t] += ds * widen_bf16(drow[t]);"),
+    "dK from dO": ("ok[t] += sc * ds * widen_bf16(qrow[t]);",
+                   "ok[t] += sc * ds * widen_bf16(drow[t]); (void)qrow;"),
+    "delta without O": ("acc += widen_bf16(dout[r * d_h + t]) * o[r * d_h + t];",
+                        "acc += widen_bf16(dout[r * d_h + t]);"),
     "kv head h mod n_kv": ("const int64_t kvh = h / g;", "const int64_t kvh = h % n_kv;"),
     "log2 in lse": ("*lse = m + log(total);", "*lse = m + log2(total);"),
     "K read transposed": ("dot += elem(kind, q, qrow + t, dq) * elem(kind, k, krow + t, dk);",
@@ -142,8 +153,29 @@ def _check_fp8(lib):
     return True
 
 
+def _check_bwd(lib):
+    # the gradients against torch autograd through SDPA in fp64 (GQA, both
+    # masks)
+    torch = pytest.importorskip("torch")
+    B, L, n_q, n_kv, d = 1, 19, 4, 2, 8
+    q, k, v = inputs.make_qkv(B, L, n_q, n_kv, d, 87)
+    do = inputs.make_qkv(B, L, n_q, n_kv, d, 88)[0]
+    for causal in (1, 0):
+        dq, dk, dv, _, _ = oracle.attention_bwd(q, k, v, do, 0.4, causal, lib=lib)
+        t = lambda x: torch.from_numpy(_vals(x)).requires_grad_(True)
+        tq, tk, tv = t(q), t(k), t(v)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk.repeat_interleave(2, 1), tv.repeat_interleave(2, 1), is_causal=bool(causal),
+            scale=float(np.float32(0.4)))
+        o.backward(torch.from_numpy(_vals(do)))
+        for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+            if not np.max(np.abs(mine - ref.numpy())) <= 1e-12:
+                return False
+    return True
+
+
 CHECKS = [_check_brute, _check_large_scores, _check_constant_v,
-          _check_zero_query, _check_flops, _check_chunk_brute, _check_fp8]
+          _check_zero_query, _check_flops, _check_chunk_brute, _check_fp8, _check_bwd]
 
 
 def _build_variant(tmp_path, name, src):
