@@ -4,7 +4,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "attn_prefill.hip"), os.path.join(PKG, "csrc", "attn_fp8.hip")]
+SRCS = [os.path.join(PKG, "csrc", name) for name in ("attn_prefill.hip", "attn_fp8.hip", "attn_bwd.hip")]
 SRC = SRCS[0]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_prefill.so")

@@ -50,6 +50,9 @@ def library():
         lib.attn_prefill_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci,
                                              ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                              ctypes.c_float, ci, vp]
+        lib.attn_prefill_bwd.restype = ci
+        lib.attn_prefill_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci,
+                                         ci, ctypes.c_float, ci, vp]
         lib.attn_decode_fwd.restype = ci
         lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ctypes.c_longlong, ci, ci, ci,
                                         ctypes.c_float, vp, ctypes.c_size_t, vp]
@@ -103,6 +106,16 @@ def fwd_fp8_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, Lq, Lk, q_offset, n_q,
         ctypes.c_void_p(out_ptr), ctypes.c_void_p(lse_ptr), int(B), int(Lq), int(Lk),
         int(q_offset), int(n_q), int(n_kv), int(d_h), float(scale), float(descale_q),
         float(descale_k), float(descale_v), int(causal), ctypes.c_void_p(stream_ptr))
+
+
+def bwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, dout_ptr, dq_ptr, dk_ptr, dv_ptr, delta_ptr,
+            B, L, n_q, n_kv, d_h, scale, causal, stream_ptr):
+    """Direct call of attn_prefill_bwd with integer pointers; returns status."""
+    vp = ctypes.c_void_p
+    return library().attn_prefill_bwd(
+        vp(q_ptr), vp(k_ptr), vp(v_ptr), vp(out_ptr), vp(lse_ptr), vp(dout_ptr), vp(dq_ptr),
+        vp(dk_ptr), vp(dv_ptr), vp(delta_ptr), int(B), int(L), int(n_q), int(n_kv), int(d_h),
+        float(scale), int(causal), vp(stream_ptr))
 
 
 def decode_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, Lk, kv_capacity, n_q, n_kv, d_h, scale,
@@ -357,3 +370,34 @@ def attn_prefill_fp8(q, k, v, descale_q, descale_k, descale_v, q_offset=0, scale
     lse = torch.empty((B, n_q, Lq), dtype=torch.float32, device=q.device)
     return attn_prefill_fp8_into(q, k, v, out, lse, descale_q, descale_k, descale_v,
                                  q_offset=q_offset, scale=scale, causal=causal, stream=stream)
+
+
+def attn_prefill_backward(q, k, v, out, lse, dout, scale=None, causal=True, stream=None,
+                          grads=None):
+    """Backward pass (see attn_prefill_bwd): q, out, dout bf16 [B, n_q, L, d_h];
+    k, v bf16 [B, n_kv, L, d_h]; lse fp32 [B, n_q, L] from the forward pass.
+    Returns (dq, dk, dv, delta); grads = (dq, dk, dv, delta) reuses buffers."""
+    import torch
+    B, n_q, n_kv, L, d_h = _check(q, k, v)
+    for name, t in (("out", out), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or \
+                tuple(t.shape) != tuple(q.shape) or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor shaped like q")
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or \
+            tuple(lse.shape) != (B, n_q, L) or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor [B, n_q, L]")
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 torch.empty((B, n_q, L), dtype=torch.float32, device=q.device))
+    dq, dk, dv, delta = grads
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_h)
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        status = bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                         lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                         dv.data_ptr(), delta.data_ptr(), B, L, n_q, n_kv, d_h, scale,
+                         int(bool(causal)), s.cuda_stream)
+    if status != ATTN_PREFILL_OK:
+        raise AttnPrefillError(status, strerror(status))
+    return dq, dk, dv, delta

@@ -1,0 +1,567 @@
+// attn_bwd.hip -- backward pass of causal GQA prefill attention for gfx950.
+//
+// The gradients of O with respect to Q, K and V for an upstream gradient dO,
+// recomputed from the forward pass's row statistic LSE instead of a stored
+// score matrix ("Long-Context Attention Explained", section "What
+// FlashAttention does not change").  With P_ij = exp(s_ij - LSE_i),
+// s_ij = scale q_i . k_j over the visible keys:
+//     D_i   = dO_i . O_i
+//     dV_j  = sum_i P_ij dO_i                 (over the group's query heads)
+//     dS_ij = P_ij (dO_i . v_j - D_i)
+//     dQ_i  = scale sum_j dS_ij k_j
+//     dK_j  = scale sum_i dS_ij q_i           (over the group's query heads)
+//
+// Three kernels, no atomics:
+//  * bwd_delta_kernel: D for every row (HBM-bound).
+//  * bwd_dkdv_kernel: work item = (b, kv-head, 128-key block); four waves,
+//    32 keys each, stream 32-row tiles of Q and dO (and the rows' LSE and D)
+//    of every query head of the group through LDS and accumulate dK^T and
+//    dV^T in registers.  Per tile and wave: S = Q K^T and dP = dO V^T with
+//    queries as rows, so the accumulator holds one key per lane and 16
+//    queries in the slot order of the B operand; then dV^T += dO^T P and
+//    dK^T += Q^T dS with dO^T and Q^T read from LDS by the transpose read.
+//  * bwd_dq_kernel: work item and query columns as the forward kernel; each
+//    wave keeps its 32 rows of Q and dO in registers and streams K and V
+//    tiles: S^T = K Q^T, dP^T = V dO^T (one query per lane), then
+//    dQ^T += K^T dS^T with K^T from the transpose read.
+// P and dS are rounded to bf16 (nearest even) for the products, everything
+// accumulates in fp32, and the gradients are rounded to bf16 once.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "attn_prefill.h"
+#include "device_common.h"
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBD = 128;          // head size
+constexpr int kBRowB = 2 * kBD;   // bytes per bf16 row
+
+// 16-byte chunk swizzles of 256-byte rows: "row" for tiles read by 16-byte
+// row reads (16 lanes take 16 consecutive rows at one chunk), "tr" for tiles
+// read by the transpose read (32 lanes take 4 rows x 2 chunk pairs).
+__device__ __forceinline__ int swz_row(int row) { return row & 15; }
+__device__ __forceinline__ int swz_tr(int row) { return (row & 3) << 2; }
+
+// A 16-byte operand fragment of row `row` (relative to a tile at `base`),
+// logical chunk `chunk`, under swizzle `swz`.
+__device__ __forceinline__ bf16x8 frag16(LDS_AS const unsigned char* base, int row, int chunk,
+                                         int swz) {
+  return *reinterpret_cast<const LDS_AS bf16x8*>(base + row * kBRowB + ((chunk ^ swz) << 4));
+}
+
+// Transposed operand: for lanes l (hi = l / 32) of a 32-row block at `base`
+// (rows = the contraction dimension, in the slot order 16 ks + 8 (s / 4) +
+// 4 hi + s % 4), the 8 values of column 32 tb + l % 32 for k-step ks.
+// In each group of 16 lanes, lane 4 r + qq supplies four consecutive 16-bit
+// values of row r and lane i receives column i of the four rows.
+__device__ __forceinline__ bf16x8 frag_tr(LDS_AS const unsigned char* base, int tb, int ks,
+                                          int lane) {
+  const int hi = lane >> 5;
+  const int tr_r = (lane >> 2) & 3;
+  const int tr_q = lane & 3;
+  const int tr_g = (lane >> 4) & 1;
+  const int t = 32 * tb + 16 * tr_g + 4 * tr_q;
+  const int key = 16 * ks + 4 * hi + tr_r;
+  const LDS_AS unsigned char* p =
+      base + key * kBRowB + (((t >> 3) ^ swz_tr(key)) << 4) + ((t >> 2) & 1) * 8;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
+  const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 8 * kBRowB));
+  return __builtin_bit_cast(
+      bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                      __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]});
+}
+
+// Source offsets of one wave's share of a tile load (rows of 256 bytes,
+// `loads` loads of 1 KB starting at LDS byte 1 KB * first), placing logical
+// chunk c of row r at physical chunk c ^ swz(r).
+template <bool TR>
+__device__ __forceinline__ int tile_src(int first, int s, int lane) {
+  const int byte = (first + s) * 1024 + lane * 16;
+  const int row = byte / kBRowB;
+  const int pos = (byte % kBRowB) >> 4;
+  return row * kBRowB + ((pos ^ (TR ? swz_tr(row) : swz_row(row))) << 4);
+}
+
+// ---- D_i = dO_i . O_i, fp32: 16 lanes per row (8 elements each)
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const unsigned short* __restrict__ out,
+                                                        const unsigned short* __restrict__ dout,
+                                                        float* __restrict__ delta,
+                                                        long long rows) {
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = gid >> 4;
+  const int part = threadIdx.x & 15;
+  float acc = 0.0f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(out + row * kBD + part * 8);
+    const u32x4 d = *reinterpret_cast<const u32x4*>(dout + row * kBD + part * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // copy the element out first: a bit cast of an ext-vector element
+      // itself compiled to a cast of element 0 on this toolchain
+      const unsigned ae = a[e], de = d[e];
+      const bf16x2 x = __builtin_bit_cast(bf16x2, ae);
+      const bf16x2 y = __builtin_bit_cast(bf16x2, de);
+      acc = fmaf((float)x[0], (float)y[0], acc);
+      acc = fmaf((float)x[1], (float)y[1], acc);
+    }
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 16);
+  if (row < rows && part == 0) delta[row] = acc;
+}
+
+// ---- dK, dV
+constexpr int kKvWaves = 4;                    // 32 keys per wave
+constexpr int kKvKeys = 32 * kKvWaves;         // keys per work item
+constexpr int kQT = 32;                        // query rows per tile
+
+__global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
+    const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+    const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta,
+    unsigned short* __restrict__ dk, unsigned short* __restrict__ dv, int L, int n_q, int n_kv,
+    int n_kblk, float scale, int causal) {
+  constexpr int D = kBD;
+  constexpr int ROWB = kBRowB;
+  constexpr int KSTEPS = D / 16;
+  constexpr int TBLK = D / 32;
+  constexpr int KV_BYTES = kKvKeys * ROWB;        // 32 KB: the item's K (or V) rows
+  constexpr int QT_BYTES = kQT * ROWB;            // 8 KB: one Q (or dO) tile
+  constexpr int KOFF = 0, VOFF = KV_BYTES;
+  constexpr int QOFF = 2 * KV_BYTES;              // 2 buffers of Q tiles
+  constexpr int DOOFF = QOFF + 2 * QT_BYTES;      // 2 buffers of dO tiles
+  constexpr int STOFF = DOOFF + 2 * QT_BYTES;     // 2 buffers x (64 lse + 64 delta) floats
+  constexpr int SMEM = STOFF + 2 * 2 * 64 * 4;
+  constexpr int KV_LOADS = KV_BYTES / (kKvWaves * 1024);   // 8 per wave
+  constexpr int QT_LOADS = QT_BYTES / (kKvWaves * 1024);   // 2 per wave
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+  LDS_AS unsigned char* const sl = (LDS_AS unsigned char*)smem;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hi = lane >> 5;
+  const int col = lane & 31;
+
+  // work item: key blocks in order (block 0, the one most queries see, first)
+  const int item = blockIdx.x;
+  const int kb = item / (gridDim.x / n_kblk);
+  const int rest = item % (gridDim.x / n_kblk);
+  const int kvh = rest % n_kv;
+  const int b = rest / n_kv;
+  const int g = n_q / n_kv;
+  const int k0 = kb * kKvKeys;
+  const int kw0 = k0 + 32 * wave;                 // this wave's first key
+
+  const unsigned short* kbase = k + ((size_t)b * n_kv + kvh) * (size_t)L * D;
+  const unsigned short* vbase = v + ((size_t)b * n_kv + kvh) * (size_t)L * D;
+
+  // the item's K and V rows into LDS (rows past L read as zero)
+  {
+    int src[KV_LOADS];
+#pragma unroll
+    for (int s = 0; s < KV_LOADS; ++s) src[s] = tile_src<false>(wave * KV_LOADS, s, lane);
+    dma_tile(kbase, src, KV_LOADS, ROWB, k0, L, kKvKeys,
+             smem + KOFF + wave * KV_LOADS * 1024);
+    dma_tile(vbase, src, KV_LOADS, ROWB, k0, L, kKvKeys,
+             smem + VOFF + wave * KV_LOADS * 1024);
+  }
+  int qsrc[QT_LOADS];
+#pragma unroll
+  for (int s = 0; s < QT_LOADS; ++s) qsrc[s] = tile_src<true>(wave * QT_LOADS, s, lane);
+
+  // query tiles: every head of the group, rows from the first tile that can
+  // see a key of the block (causal) or from 0
+  const int qt_first = causal ? k0 / kQT : 0;
+  const int qt_per_head = (L + kQT - 1) / kQT - qt_first;
+  const int n_qt = g * qt_per_head;
+  auto tile_rows = [&] __device__ (int n, int& h, int& q0) __attribute__((always_inline)) {
+    h = kvh * g + n / qt_per_head;
+    q0 = (qt_first + n % qt_per_head) * kQT;
+  };
+  // loads of tile n into buffer n % 2: Q and dO rows (zero past L), and the
+  // rows' LSE and delta (wave 0, 4 bytes per lane; zero past L)
+  auto load_qtile = [&] __device__ (int n) __attribute__((always_inline)) {
+    int h, q0;
+    tile_rows(n, h, q0);
+    const size_t rowbase = ((size_t)b * n_q + h) * (size_t)L;
+    const int buf = n & 1;
+    dma_tile(q + rowbase * D, qsrc, QT_LOADS, ROWB, q0, L, kQT,
+             smem + QOFF + buf * QT_BYTES + wave * QT_LOADS * 1024);
+    dma_tile(dout + rowbase * D, qsrc, QT_LOADS, ROWB, q0, L, kQT,
+             smem + DOOFF + buf * QT_BYTES + wave * QT_LOADS * 1024);
+    if (wave == 0) {
+      const int lim = max(min(L - q0, 64), 0) * 4;
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + rowbase + q0, (unsigned)lim);
+      const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + rowbase + q0, (unsigned)lim);
+      LDS_AS unsigned char* st = sl + STOFF + buf * 512;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (LDS_AS void*)(st), 4, lane * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (LDS_AS void*)(st + 256), 4, lane * 4, 0, 0,
+                                               0);
+    }
+  };
+
+  f32x16 dkT[TBLK], dvT[TBLK];
+#pragma unroll
+  for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dkT[tb][r] = dvT[tb][r] = 0.0f;
+  const float c2 = scale * kLog2e;
+
+  if (n_qt > 0) load_qtile(0);
+  for (int n = 0; n < n_qt; ++n) {
+    // tile n has landed everywhere, and every wave is done with tile n - 1
+    wait_vmcnt<0>();
+    tile_barrier();
+    if (n + 1 < n_qt) load_qtile(n + 1);
+    int h, q0;
+    tile_rows(n, h, q0);
+    (void)h;
+    const int buf = n & 1;
+    // skip when every query of the tile is before every key of the wave
+    if (causal && q0 + kQT - 1 < kw0) continue;
+    LDS_AS const unsigned char* qt = sl + QOFF + buf * QT_BYTES;
+    LDS_AS const unsigned char* dot = sl + DOOFF + buf * QT_BYTES;
+    LDS_AS const unsigned char* kt = sl + KOFF + 32 * wave * ROWB;
+    LDS_AS const unsigned char* vt = sl + VOFF + 32 * wave * ROWB;
+    LDS_AS const float* st = (LDS_AS const float*)(sl + STOFF + buf * 512);
+
+    // S = Q K^T and dP = dO V^T: rows = queries (A from the Q / dO tile),
+    // columns = this wave's keys (B from its K / V rows)
+    f32x16 S, dP;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int ch = 2 * kk + hi;
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(qt, col, ch, swz_tr(col)),
+                                                 frag16(kt, col, ch, swz_row(col)), S, 0, 0, 0);
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(dot, col, ch, swz_tr(col)),
+                                                  frag16(vt, col, ch, swz_row(col)), dP, 0, 0,
+                                                  0);
+    }
+    // P = 2^(c2 s - log2e lse), dS = P (dP - D); lane (key col) holds
+    // queries 8 (r / 4) + 4 hi + r % 4
+    bf16x8 pk[2], dsk[2];
+    const int key = kw0 + col;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const f32x4 l4 = *reinterpret_cast<const LDS_AS f32x4*>(st + 8 * a + 4 * hi);
+      const f32x4 d4 = *reinterpret_cast<const LDS_AS f32x4*>(st + 64 + 8 * a + 4 * hi);
+      const float lv[4] = {l4[0], l4[1], l4[2], l4[3]};
+      const float dv4[4] = {d4[0], d4[1], d4[2], d4[3]};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int r = 4 * a + c;
+        const int qi = q0 + 8 * a + 4 * hi + c;
+        const bool dead = (causal && key > qi) || key >= L;
+        const float p = dead ? 0.0f : __builtin_amdgcn_exp2f(fmaf(S[r], c2, -lv[c] * kLog2e));
+        const float ds = p * (dP[r] - dv4[c]);
+        pk[r >> 3][r & 7] = (__bf16)p;
+        dsk[r >> 3][r & 7] = (__bf16)ds;
+      }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS (contraction over the tile's queries)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int tb = 0; tb < TBLK; ++tb) {
+        dvT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(dot, tb, ks, lane), pk[ks],
+                                                         dvT[tb], 0, 0, 0);
+        dkT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(qt, tb, ks, lane), dsk[ks],
+                                                         dkT[tb], 0, 0, 0);
+      }
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue: dK = scale dK^T^T, dV = dV^T^T in bf16, staged through
+  // LDS as whole rows (the Q/dO buffers and K rows are free now)
+  tile_barrier();
+  LDS_AS unsigned char* ot = sl + wave * 2 * 32 * ROWB;   // 16 KB per wave: dK rows, dV rows
+#pragma unroll
+  for (int which = 0; which < 2; ++which)
+#pragma unroll
+    for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o4[e] = (__bf16)(which == 0 ? dkT[tb][grp * 4 + e] * scale : dvT[tb][grp * 4 + e]);
+        const int chunk = tb * 4 + grp;
+        *reinterpret_cast<LDS_AS u32x2*>(ot + which * 32 * ROWB + col * ROWB +
+                                         ((chunk ^ swz_row(col)) << 4) + hi * 8) =
+            __builtin_bit_cast(u32x2, o4);
+      }
+  // a wave reads back only the rows it wrote: no barrier needed
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    unsigned short* gbase = (which == 0 ? dk : dv) + (((size_t)b * n_kv + kvh) * L + kw0) * D;
+#pragma unroll
+    for (int st = 0; st < 32 * ROWB / 1024; ++st) {
+      const int byte = st * 1024 + lane * 16;
+      const int row = byte / ROWB;
+      const int chunk = (byte % ROWB) >> 4;
+      const u32x4 v4 = *reinterpret_cast<const LDS_AS u32x4*>(
+          ot + which * 32 * ROWB + row * ROWB + ((chunk ^ swz_row(row)) << 4));
+      if (kw0 + row < L)
+        *reinterpret_cast<u32x4*>(gbase + (size_t)row * D + chunk * 8) = v4;
+    }
+  }
+}
+
+// ---- dQ
+constexpr int kDqCols = 256;   // query columns per workgroup (8 waves x 32)
+constexpr int kDqWaves = 8;
+constexpr int kDqKeys = 64;    // keys per K/V tile
+
+template <int HWG>
+__global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
+    const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+    const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta,
+    unsigned short* __restrict__ dq, int L, int n_q, int n_kv, int n_qblk, int items_per_qblk,
+    float scale, int causal) {
+  constexpr int D = kBD;
+  constexpr int ROWB = kBRowB;
+  constexpr int KSTEPS = D / 16;
+  constexpr int TBLK = D / 32;
+  constexpr int BR = kDqCols / HWG;
+  constexpr int TILE = kDqKeys * ROWB;                  // 16 KB
+  constexpr int LOADS = TILE / (kDqWaves * 1024);       // 2 per wave
+  constexpr int KOFF = 0, VOFF = 2 * TILE;              // two buffers each
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE];
+  LDS_AS unsigned char* const sl = (LDS_AS unsigned char*)smem;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hi = lane >> 5;
+  const int col = lane & 31;
+
+  const int item = blockIdx.x;
+  const int qb = n_qblk - 1 - item / items_per_qblk;
+  int rest = item % items_per_qblk;
+  const int g = n_q / n_kv;
+  const int ngroups = g / HWG;
+  const int hg = rest % ngroups;
+  rest /= ngroups;
+  const int kvh = rest % n_kv;
+  const int b = rest / n_kv;
+  const int c0 = 32 * wave;
+  const int hh = kvh * g + hg * HWG + c0 / BR;
+  const int q0 = qb * BR + c0 % BR;
+  const int qi = q0 + col;
+
+  const size_t rowbase = ((size_t)b * n_q + hh) * (size_t)L;
+  const unsigned short* kbase = k + ((size_t)b * n_kv + kvh) * (size_t)L * D;
+  const unsigned short* vbase = v + ((size_t)b * n_kv + kvh) * (size_t)L * D;
+
+  const int wg_end = min(qb * BR + BR, L);
+  const int n_tiles = causal ? (wg_end + kDqKeys - 1) / kDqKeys : (L + kDqKeys - 1) / kDqKeys;
+  const int last_row = q0 < L ? min(q0 + 31, L - 1) : -1;
+  const int wave_tiles = last_row < 0 ? 0 : (causal ? last_row / kDqKeys + 1 : n_tiles);
+
+  // Q and dO rows of the wave's 32 columns as B operands (zero past L)
+  bf16x8 qf[KSTEPS], of[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+    if (qi < L) {
+      a = *reinterpret_cast<const u32x4*>(q + (rowbase + qi) * D + kk * 16 + hi * 8);
+      c = *reinterpret_cast<const u32x4*>(dout + (rowbase + qi) * D + kk * 16 + hi * 8);
+    }
+    qf[kk] = __builtin_bit_cast(bf16x8, a);
+    of[kk] = __builtin_bit_cast(bf16x8, c);
+  }
+  const float lse2 = qi < L ? lse[rowbase + qi] * kLog2e : 0.0f;
+  const float dlt = qi < L ? delta[rowbase + qi] : 0.0f;
+
+  int ksrc[LOADS], vsrc[LOADS];
+#pragma unroll
+  for (int s = 0; s < LOADS; ++s) {
+    ksrc[s] = tile_src<true>(wave * LOADS, s, lane);    // K: row reads and transpose reads
+    vsrc[s] = tile_src<false>(wave * LOADS, s, lane);   // V: row reads
+  }
+  auto load_tiles = [&] __device__ (int t) __attribute__((always_inline)) {
+    const int buf = t & 1;
+    dma_tile(kbase, ksrc, LOADS, ROWB, t * kDqKeys, L, kDqKeys,
+             smem + KOFF + buf * TILE + wave * LOADS * 1024);
+    dma_tile(vbase, vsrc, LOADS, ROWB, t * kDqKeys, L, kDqKeys,
+             smem + VOFF + buf * TILE + wave * LOADS * 1024);
+  };
+
+  f32x16 dqT[TBLK];
+#pragma unroll
+  for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqT[tb][r] = 0.0f;
+  const float c2 = scale * kLog2e;
+
+  if (n_tiles > 0) load_tiles(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    wait_vmcnt<0>();
+    tile_barrier();
+    if (t + 1 < n_tiles) load_tiles(t + 1);
+    if (t >= wave_tiles) continue;
+    const int buf = t & 1;
+    LDS_AS const unsigned char* kt = sl + KOFF + buf * TILE;
+    LDS_AS const unsigned char* vt = sl + VOFF + buf * TILE;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      const int j0 = t * kDqKeys + 32 * jb;
+      LDS_AS const unsigned char* kh = kt + 32 * jb * ROWB;
+      LDS_AS const unsigned char* vh = vt + 32 * jb * ROWB;
+      // S^T = K Q^T and dP^T = V dO^T: rows = keys, columns = queries
+      f32x16 S, dP;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const int ch = 2 * kk + hi;
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(kh, col, ch, swz_tr(col)), qf[kk], S,
+                                                   0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(vh, col, ch, swz_row(col)), of[kk],
+                                                    dP, 0, 0, 0);
+      }
+      // dS^T = P^T (dP^T - D), lane (query col) holds keys 8 (r / 4) + 4 hi + r % 4
+      bf16x8 dsk[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + (r >> 2) * 8 + hi * 4 + (r & 3);
+        const bool dead = (causal && j > qi) || j >= L;
+        const float p = dead ? 0.0f : __builtin_amdgcn_exp2f(fmaf(S[r], c2, -lse2));
+        dsk[r >> 3][r & 7] = (__bf16)(p * (dP[r] - dlt));
+      }
+      // dQ^T += K^T dS^T (contraction over the half's keys)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int tb = 0; tb < TBLK; ++tb)
+          dqT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(kh, tb, ks, lane), dsk[ks],
+                                                           dqT[tb], 0, 0, 0);
+    }
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue: dQ = scale dQ^T^T in bf16, staged through LDS as whole rows
+  tile_barrier();
+  LDS_AS unsigned char* ot = sl + wave * 32 * ROWB;   // 8 KB per wave
+#pragma unroll
+  for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      bf16x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(dqT[tb][grp * 4 + e] * scale);
+      const int chunk = tb * 4 + grp;
+      *reinterpret_cast<LDS_AS u32x2*>(ot + col * ROWB + ((chunk ^ swz_row(col)) << 4) +
+                                       hi * 8) = __builtin_bit_cast(u32x2, o4);
+    }
+  unsigned short* obase = dq + (rowbase + q0) * D;
+#pragma unroll
+  for (int st = 0; st < 32 * ROWB / 1024; ++st) {
+    const int byte = st * 1024 + lane * 16;
+    const int row = byte / ROWB;
+    const int chunk = (byte % ROWB) >> 4;
+    const u32x4 v4 =
+        *reinterpret_cast<const LDS_AS u32x4*>(ot + row * ROWB + ((chunk ^ swz_row(row)) << 4));
+    if (q0 + row < L) *reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8) = v4;
+  }
+}
+
+int bwd_pick_hwg(int g) {
+  if (g % 8 == 0) return 8;
+  if (g % 4 == 0) return 4;
+  if (g % 2 == 0) return 2;
+  return 1;
+}
+
+template <int HWG>
+int launch_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+              const float* delta, void* dq, int B, int L, int n_q, int n_kv, float scale,
+              int causal, hipStream_t stream) {
+  constexpr int BR = kDqCols / HWG;
+  const int n_qblk = (L + BR - 1) / BR;
+  const long long items_per_qblk = (long long)B * n_kv * ((n_q / n_kv) / HWG);
+  const long long grid = items_per_qblk * n_qblk;
+  if (items_per_qblk > INT_MAX || grid > INT_MAX) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  hipLaunchKernelGGL((bwd_dq_kernel<HWG>), dim3((unsigned)grid), dim3(64 * kDqWaves), 0, stream,
+                     static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
+                     static_cast<const unsigned short*>(v),
+                     static_cast<const unsigned short*>(dout), lse, delta,
+                     static_cast<unsigned short*>(dq), L, n_q, n_kv, n_qblk,
+                     (int)items_per_qblk, scale, causal);
+  return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* out,
+                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                float* delta, int B, int L, int n_q, int n_kv, int d_h,
+                                float scale, int causal, hipStream_t stream) {
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !delta)
+    return ATTN_PREFILL_ERR_NULL_PTR;
+  if (B < 1 || L < 1 || n_q < 1 || n_kv < 1) return ATTN_PREFILL_ERR_BAD_SHAPE;
+  if (n_q % n_kv != 0) return ATTN_PREFILL_ERR_BAD_GQA;
+  if (d_h != kBD) return ATTN_PREFILL_ERR_BAD_HEADDIM;
+  if (!std::isfinite(scale)) return ATTN_PREFILL_ERR_BAD_SCALE;
+  if (causal != 0 && causal != 1) return ATTN_PREFILL_ERR_BAD_CAUSAL;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                          reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out) |
+                          reinterpret_cast<uintptr_t>(dout) | reinterpret_cast<uintptr_t>(dq) |
+                          reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv);
+  if ((align & 15) != 0 ||
+      ((reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(delta)) & 3) != 0)
+    return ATTN_PREFILL_ERR_MISALIGNED;
+  size_t rows, q_elems, kv_elems;
+  if (__builtin_mul_overflow((size_t)B, (size_t)n_q, &rows) ||
+      __builtin_mul_overflow(rows, (size_t)L, &rows) ||
+      __builtin_mul_overflow(rows, (size_t)d_h, &q_elems) ||
+      __builtin_mul_overflow((size_t)B, (size_t)n_kv, &kv_elems) ||
+      __builtin_mul_overflow(kv_elems, (size_t)L, &kv_elems) ||
+      __builtin_mul_overflow(kv_elems, (size_t)d_h, &kv_elems) ||
+      q_elems > ((size_t)1 << 61) || kv_elems > ((size_t)1 << 61))
+    return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  const size_t qb = q_elems * 2, kvb = kv_elems * 2, lb = rows * 4;
+  // the outputs may overlap nothing
+  const void* outs[4] = {dq, dk, dv, delta};
+  const size_t osz[4] = {qb, kvb, kvb, lb};
+  const void* ins[6] = {q, k, v, out, lse, dout};
+  const size_t isz[6] = {qb, kvb, kvb, qb, lb, qb};
+  for (int a = 0; a < 4; ++a) {
+    for (int c = 0; c < 6; ++c)
+      if (overlaps(outs[a], osz[a], ins[c], isz[c])) return ATTN_PREFILL_ERR_ALIASING;
+    for (int c = a + 1; c < 4; ++c)
+      if (overlaps(outs[a], osz[a], outs[c], osz[c])) return ATTN_PREFILL_ERR_ALIASING;
+  }
+  const long long n_kblk = ((long long)L + kKvKeys - 1) / kKvKeys;
+  const long long kv_grid = (long long)B * n_kv * n_kblk;
+  const long long delta_blocks = ((long long)rows * 16 + 255) / 256;
+  if (kv_grid > INT_MAX || delta_blocks > INT_MAX) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+
+  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)delta_blocks), dim3(256), 0, stream,
+                     static_cast<const unsigned short*>(out),
+                     static_cast<const unsigned short*>(dout), delta, (long long)rows);
+  if (hipGetLastError() != hipSuccess) return ATTN_PREFILL_ERR_LAUNCH;
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_grid), dim3(64 * kKvWaves), 0, stream,
+                     static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
+                     static_cast<const unsigned short*>(v),
+                     static_cast<const unsigned short*>(dout), lse, delta,
+                     static_cast<unsigned short*>(dk), static_cast<unsigned short*>(dv), L, n_q,
+                     n_kv, (int)n_kblk, scale, causal);
+  if (hipGetLastError() != hipSuccess) return ATTN_PREFILL_ERR_LAUNCH;
+  switch (bwd_pick_hwg(n_q / n_kv)) {
+    case 8: return launch_dq<8>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);
+    case 4: return launch_dq<4>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);
+    case 2: return launch_dq<2>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);
+    default: return launch_dq<1>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);
+  }
+}

@@ -166,6 +166,35 @@ int attn_prefill_fwd_fp8(const void *q, const void *k, const void *v, void *out,
                          int causal, hipStream_t stream);
 
 /*
+ * Backward pass: the gradients of O with respect to Q, K and V for an
+ * upstream gradient dO, recomputed from the forward pass's LSE instead of a
+ * stored score matrix ("Long-Context Attention Explained", section "What
+ * FlashAttention does not change").  With P_ij = exp(s_ij - LSE_i) over the
+ * visible keys:
+ *     delta_i = dO_i . O_i
+ *     dV_j = sum_i P_ij dO_i,  dS_ij = P_ij (dO_i . v_j - delta_i)
+ *     dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i
+ * dK and dV sum over the g query heads of each key/value head.
+ *   q, out, dout : device pointers, bf16 [B, n_q, L, d_h] (out is the
+ *                  forward output)
+ *   k, v         : device pointers, bf16 [B, n_kv, L, d_h]
+ *   lse          : device pointer, fp32 [B, n_q, L], the forward LSE
+ *   dq           : device pointer, bf16 [B, n_q, L, d_h], written entirely
+ *   dk, dv       : device pointers, bf16 [B, n_kv, L, d_h], written entirely
+ *   delta        : device pointer, fp32 [B, n_q, L], written (delta_i)
+ *   d_h must be 128; other arguments as attn_prefill_fwd.
+ * Numerics: P is recomputed in fp32 from lse, delta from the bf16 out; P and
+ * dS are rounded to bf16 (nearest even) for the matrix-core products, which
+ * accumulate in fp32; the gradients are rounded to bf16 once.  The outputs
+ * may not overlap each other or any input.  Errors as for attn_prefill_fwd
+ * (ATTN_PREFILL_ERR_BAD_HEADDIM for d_h != 128).
+ */
+int attn_prefill_bwd(const void *q, const void *k, const void *v, const void *out,
+                     const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                     float *delta, int B, int L, int n_q, int n_kv, int d_h, float scale,
+                     int causal, hipStream_t stream);
+
+/*
  * Decode: one new query per sequence against the sequence's whole K/V cache.
  * The query is token Lk - 1 of its sequence, its own key and value already in
  * the cache, so it sees every cached key; attention becomes a matrix-vector

@@ -60,17 +60,17 @@ def load_library(path):
     lib.oracle_attn_bwd_rowstats.restype = ctypes.c_int
     lib.oracle_attn_bwd_rowstats.argtypes = [
         u16p, u16p, u16p, u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, ctypes.c_int]
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, dp, ctypes.c_int]
     lib.oracle_attn_bwd_dq.restype = ctypes.c_int
     lib.oracle_attn_bwd_dq.argtypes = [
         u16p, u16p, u16p, u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, i64p,
-        ctypes.c_int64, dp, ctypes.c_int]
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, dp, i64p,
+        ctypes.c_int64, dp, dp, ctypes.c_int]
     lib.oracle_attn_bwd_dkdv.restype = ctypes.c_int
     lib.oracle_attn_bwd_dkdv.argtypes = [
         u16p, u16p, u16p, u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, i64p,
-        ctypes.c_int64, dp, dp, ctypes.c_int]
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, dp, i64p,
+        ctypes.c_int64, dp, dp, dp, dp, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_version.restype = ctypes.c_int
     return lib
@@ -282,61 +282,75 @@ def _bwd_shapes(q, k, v, dout):
     return q, k, v, dout, B, n_q, n_kv, L, d
 
 
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
 def attention_bwd_rowstats(q, k, v, dout, scale, causal=True, threads=0, lib=None):
-    """Every row's LSE and delta = dO . O (exact O), fp64 [B * n_q * L] each."""
+    """Every row's LSE, delta = dO . O (exact O) and sum_t |dO_t O_t|, fp64
+    [B * n_q * L] each."""
     q, k, v, dout, B, n_q, n_kv, L, d = _bwd_shapes(q, k, v, dout)
     lse = np.empty(B * n_q * L)
     delta = np.empty(B * n_q * L)
+    absd = np.empty(B * n_q * L)
     u16p = ctypes.POINTER(ctypes.c_uint16)
-    dp = ctypes.POINTER(ctypes.c_double)
     rc = (lib or _load()).oracle_attn_bwd_rowstats(
         q.ctypes.data_as(u16p), k.ctypes.data_as(u16p), v.ctypes.data_as(u16p),
         dout.ctypes.data_as(u16p), B, L, n_q, n_kv, d, float(np.float32(scale)), int(causal),
-        lse.ctypes.data_as(dp), delta.ctypes.data_as(dp), int(threads))
+        _ptr(lse), _ptr(delta), _ptr(absd), int(threads))
     if rc != OK:
         raise ValueError(f"oracle_attn_bwd_rowstats failed with code {rc}")
-    return lse, delta
+    return lse, delta, absd
 
 
-def attention_bwd_dq(q, k, v, dout, scale, causal, lse, delta, rows, threads=0, lib=None):
-    """dQ [len(rows), d_h] for flat query rows (b * n_q + h) * L + i."""
+def attention_bwd_dq(q, k, v, dout, scale, causal, lse, delta, rows, abs_delta=None,
+                     threads=0, lib=None):
+    """dQ [len(rows), d_h] for flat query rows (b * n_q + h) * L + i; with
+    abs_delta given also the per-element rounding bound (see the C source):
+    returns dq or (dq, bound)."""
     q, k, v, dout, B, n_q, n_kv, L, d = _bwd_shapes(q, k, v, dout)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     lse = np.ascontiguousarray(lse, dtype=np.float64)
     delta = np.ascontiguousarray(delta, dtype=np.float64)
+    absd = None if abs_delta is None else np.ascontiguousarray(abs_delta, dtype=np.float64)
     out = np.empty((rows.size, d))
+    bound = None if absd is None else np.empty((rows.size, d))
     u16p = ctypes.POINTER(ctypes.c_uint16)
-    dp = ctypes.POINTER(ctypes.c_double)
     rc = (lib or _load()).oracle_attn_bwd_dq(
         q.ctypes.data_as(u16p), k.ctypes.data_as(u16p), v.ctypes.data_as(u16p),
         dout.ctypes.data_as(u16p), B, L, n_q, n_kv, d, float(np.float32(scale)), int(causal),
-        lse.ctypes.data_as(dp), delta.ctypes.data_as(dp),
+        _ptr(lse), _ptr(delta), _ptr(absd),
         rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size,
-        out.ctypes.data_as(dp), int(threads))
+        _ptr(out), _ptr(bound), int(threads))
     if rc != OK:
         raise ValueError(f"oracle_attn_bwd_dq failed with code {rc}")
-    return out
+    return out if bound is None else (out, bound)
 
 
-def attention_bwd_dkdv(q, k, v, dout, scale, causal, lse, delta, rows, threads=0, lib=None):
-    """(dK, dV) [len(rows), d_h] for flat key rows (b * n_kv + kvh) * L + j."""
+def attention_bwd_dkdv(q, k, v, dout, scale, causal, lse, delta, rows, abs_delta=None,
+                       threads=0, lib=None):
+    """(dK, dV) [len(rows), d_h] for flat key rows (b * n_kv + kvh) * L + j;
+    with abs_delta given also their rounding bounds: (dk, dv, bound_dk,
+    bound_dv)."""
     q, k, v, dout, B, n_q, n_kv, L, d = _bwd_shapes(q, k, v, dout)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     lse = np.ascontiguousarray(lse, dtype=np.float64)
     delta = np.ascontiguousarray(delta, dtype=np.float64)
+    absd = None if abs_delta is None else np.ascontiguousarray(abs_delta, dtype=np.float64)
     dk = np.empty((rows.size, d))
     dv = np.empty((rows.size, d))
+    bk = None if absd is None else np.empty((rows.size, d))
+    bv = None if absd is None else np.empty((rows.size, d))
     u16p = ctypes.POINTER(ctypes.c_uint16)
-    dp = ctypes.POINTER(ctypes.c_double)
     rc = (lib or _load()).oracle_attn_bwd_dkdv(
         q.ctypes.data_as(u16p), k.ctypes.data_as(u16p), v.ctypes.data_as(u16p),
         dout.ctypes.data_as(u16p), B, L, n_q, n_kv, d, float(np.float32(scale)), int(causal),
-        lse.ctypes.data_as(dp), delta.ctypes.data_as(dp),
+        _ptr(lse), _ptr(delta), _ptr(absd),
         rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size,
-        dk.ctypes.data_as(dp), dv.ctypes.data_as(dp), int(threads))
+        _ptr(dk), _ptr(dv), _ptr(bk), _ptr(bv), int(threads))
     if rc != OK:
         raise ValueError(f"oracle_attn_bwd_dkdv failed with code {rc}")
-    return dk, dv
+    return (dk, dv) if bk is None else (dk, dv, bk, bv)
 
 
 def attention_bwd(q, k, v, dout, scale, causal=True, threads=0, lib=None):
@@ -344,10 +358,10 @@ def attention_bwd(q, k, v, dout, scale, causal=True, threads=0, lib=None):
     plus the row statistics (lse, delta)."""
     B, n_q, L, d = q.shape
     n_kv = k.shape[1]
-    lse, delta = attention_bwd_rowstats(q, k, v, dout, scale, causal, threads, lib)
+    lse, delta, _ = attention_bwd_rowstats(q, k, v, dout, scale, causal, threads, lib)
     dq = attention_bwd_dq(q, k, v, dout, scale, causal, lse, delta,
-                          np.arange(B * n_q * L), threads, lib)
+                          np.arange(B * n_q * L), threads=threads, lib=lib)
     dk, dv = attention_bwd_dkdv(q, k, v, dout, scale, causal, lse, delta,
-                                np.arange(B * n_kv * L), threads, lib)
+                                np.arange(B * n_kv * L), threads=threads, lib=lib)
     return (dq.reshape(B, n_q, L, d), dk.reshape(B, n_kv, L, d), dv.reshape(B, n_kv, L, d),
             lse, delta)

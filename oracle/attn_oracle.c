@@ -313,11 +313,12 @@ int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 
 /* Per-row statistics for the backward pass: lse[r] (natural log, as the
  * forward oracle) and delta[r] = sum_t dO[r,t] O[r,t] with O the exact
- * output, for every row r, in fp64. */
+ * output, for every row r, in fp64; abs_delta (NULL or [rows]) receives
+ * sum_t |dO[r,t] O[r,t]|. */
 int oracle_attn_bwd_rowstats(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                              const uint16_t *dout, int64_t B, int64_t L, int64_t n_q,
                              int64_t n_kv, int64_t d_h, float scale, int causal,
-                             double *lse, double *delta, int threads)
+                             double *lse, double *delta, double *abs_delta, int threads)
 {
     if (!dout || !delta) return ORACLE_BAD_ARG;
     const int64_t n_rows = B * n_q * L;
@@ -328,10 +329,13 @@ int oracle_attn_bwd_rowstats(const uint16_t *q, const uint16_t *k, const uint16_
                           causal, NULL, n_rows, o, lse, NULL, &flops, threads);
     if (rc == ORACLE_OK) {
         for (int64_t r = 0; r < n_rows; ++r) {
-            double acc = 0.0;
-            for (int64_t t = 0; t < d_h; ++t)
+            double acc = 0.0, mag = 0.0;
+            for (int64_t t = 0; t < d_h; ++t) {
                 acc += widen_bf16(dout[r * d_h + t]) * o[r * d_h + t];
+                mag += fabs(widen_bf16(dout[r * d_h + t]) * o[r * d_h + t]);
+            }
             delta[r] = acc;
+            if (abs_delta) abs_delta[r] = mag;
         }
     }
     free(o);
@@ -367,15 +371,47 @@ static double bwd_dp(const uint16_t *v, const uint16_t *dout, int64_t L, int64_t
     return acc;
 }
 
+/* Rounding bounds for a kernel that recomputes P in fp32 from an fp32 LSE,
+ * accumulates products of bf16 values in fp32, forms D from O rounded to
+ * bf16, rounds P and dS to bf16 (nearest even) for the products and the
+ * gradients to bf16 once:
+ *   u = 2^-8 (bf16's unit roundoff: 8 significant bits, nearest even),
+ *   eP = 2^-16 (relative error of the fp32 P),
+ *   ea = 2^-16 (an fp32 sum of up to 256 products: 256 x 2^-24),
+ *   E_ij = (u + eP) |dS_ij| + P_ij (ea sum_t |dO_it v_jt| + (u + ea) A_i),
+ *   A_i = sum_t |dO_it O_it|,
+ *   |dV_jt error| <= (u + eP + ea) sum_i P_ij |dO_it| + u |dV_jt|,
+ *   |dQ_it error| <= scale sum_j (E_ij + ea |dS_ij|) |k_jt| + u |dQ_it|,
+ *   |dK_jt error| <= scale sum_i (E_ij + ea |dS_ij|) |q_it| + u |dK_jt|. */
+static const double BWD_U = 1.0 / 256.0;
+static const double BWD_EP = 1.0 / 65536.0;
+static const double BWD_EA = 1.0 / 65536.0;
+
+/* sum_t |dO_it v_jt| */
+static double bwd_abs_dp(const uint16_t *v, const uint16_t *dout, int64_t L, int64_t n_q,
+                         int64_t n_kv, int64_t d_h, int64_t b, int64_t h, int64_t i, int64_t j)
+{
+    const int64_t kvh = h / (n_q / n_kv);
+    const uint16_t *drow = dout + ((b * n_q + h) * L + i) * d_h;
+    const uint16_t *vrow = v + ((b * n_kv + kvh) * L + j) * d_h;
+    double acc = 0.0;
+    for (int64_t t = 0; t < d_h; ++t)
+        acc += fabs(widen_bf16(drow[t]) * widen_bf16(vrow[t]));
+    return acc;
+}
+
 /* dQ for the requested query rows (flat (b * n_q + h) * L + i):
  * dq [n_rows, d_h] fp64.  lse and delta: every row's statistics, from
- * oracle_attn_bwd_rowstats. */
+ * oracle_attn_bwd_rowstats.  bound (NULL or [n_rows, d_h], then abs_delta
+ * from oracle_attn_bwd_rowstats is required) receives the rounding bound
+ * described above. */
 int oracle_attn_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                        const uint16_t *dout, int64_t B, int64_t L, int64_t n_q, int64_t n_kv,
                        int64_t d_h, float scale, int causal, const double *lse,
-                       const double *delta, const int64_t *rows, int64_t n_rows, double *dq,
-                       int threads)
+                       const double *delta, const double *abs_delta, const int64_t *rows,
+                       int64_t n_rows, double *dq, double *bound, int threads)
 {
+    if (bound && !abs_delta) return ORACLE_BAD_ARG;
     if (!q || !k || !v || !dout || !lse || !delta || !rows || !dq) return ORACLE_BAD_ARG;
     if (B < 1 || L < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || n_q % n_kv) return ORACLE_BAD_ARG;
     for (int64_t r = 0; r < n_rows; ++r)
@@ -392,14 +428,25 @@ int oracle_attn_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         const int64_t i = row % L, h = (row / L) % n_q, b = row / (L * n_q);
         const int64_t kvh = h / (n_q / n_kv);
         double *out = dq + r * d_h;
+        double *bnd = bound ? bound + r * d_h : NULL;
         for (int64_t t = 0; t < d_h; ++t) out[t] = 0.0;
+        if (bnd)
+            for (int64_t t = 0; t < d_h; ++t) bnd[t] = 0.0;
         const int64_t n_vis = causal ? i + 1 : L;
         for (int64_t j = 0; j < n_vis; ++j) {
             const double p = bwd_weight(q, k, L, n_q, n_kv, d_h, sc, causal, b, h, i, j, lse[row]);
             const double ds = p * (bwd_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j) - delta[row]);
             const uint16_t *krow = k + ((b * n_kv + kvh) * L + j) * d_h;
             for (int64_t t = 0; t < d_h; ++t) out[t] += sc * ds * widen_bf16(krow[t]);
+            if (bnd) {
+                const double e = (BWD_U + BWD_EP + BWD_EA) * fabs(ds) +
+                                 p * (BWD_EA * bwd_abs_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j) +
+                                      (BWD_U + BWD_EA) * abs_delta[row]);
+                for (int64_t t = 0; t < d_h; ++t) bnd[t] += sc * e * fabs(widen_bf16(krow[t]));
+            }
         }
+        if (bnd)
+            for (int64_t t = 0; t < d_h; ++t) bnd[t] += BWD_U * fabs(out[t]);
     }
     return ORACLE_OK;
 }
@@ -410,9 +457,11 @@ int oracle_attn_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 int oracle_attn_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const uint16_t *dout, int64_t B, int64_t L, int64_t n_q, int64_t n_kv,
                          int64_t d_h, float scale, int causal, const double *lse,
-                         const double *delta, const int64_t *rows, int64_t n_rows, double *dk,
-                         double *dv, int threads)
+                         const double *delta, const double *abs_delta, const int64_t *rows,
+                         int64_t n_rows, double *dk, double *dv, double *bound_dk,
+                         double *bound_dv, int threads)
 {
+    if ((bound_dk || bound_dv) && !(bound_dk && bound_dv && abs_delta)) return ORACLE_BAD_ARG;
     if (!q || !k || !v || !dout || !lse || !delta || !rows || !dk || !dv) return ORACLE_BAD_ARG;
     if (B < 1 || L < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || n_q % n_kv) return ORACLE_BAD_ARG;
     for (int64_t r = 0; r < n_rows; ++r)
@@ -429,7 +478,11 @@ int oracle_attn_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v
         const int64_t row = rows[r];
         const int64_t j = row % L, kvh = (row / L) % n_kv, b = row / (L * n_kv);
         double *ok = dk + r * d_h, *ov = dv + r * d_h;
+        double *bk = bound_dk ? bound_dk + r * d_h : NULL;
+        double *bv = bound_dv ? bound_dv + r * d_h : NULL;
         for (int64_t t = 0; t < d_h; ++t) ok[t] = ov[t] = 0.0;
+        if (bk)
+            for (int64_t t = 0; t < d_h; ++t) bk[t] = bv[t] = 0.0;
         for (int64_t h = kvh * g; h < kvh * g + g; ++h) {
             for (int64_t i = causal ? j : 0; i < L; ++i) {
                 const int64_t qrow_id = (b * n_q + h) * L + i;
@@ -443,8 +496,23 @@ int oracle_attn_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v
                     ov[t] += p * widen_bf16(drow[t]);
                     ok[t] += sc * ds * widen_bf16(qrow[t]);
                 }
+                if (bk) {
+                    const double e =
+                        (BWD_U + BWD_EP + BWD_EA) * fabs(ds) +
+                        p * (BWD_EA * bwd_abs_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j) +
+                             (BWD_U + BWD_EA) * abs_delta[qrow_id]);
+                    for (int64_t t = 0; t < d_h; ++t) {
+                        bk[t] += sc * e * fabs(widen_bf16(qrow[t]));
+                        bv[t] += (BWD_U + BWD_EP + BWD_EA) * p * fabs(widen_bf16(drow[t]));
+                    }
+                }
             }
         }
+        if (bk)
+            for (int64_t t = 0; t < d_h; ++t) {
+                bk[t] += BWD_U * fabs(ok[t]);
+                bv[t] += BWD_U * fabs(ov[t]);
+            }
     }
     return ORACLE_OK;
 }

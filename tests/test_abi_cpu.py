@@ -23,8 +23,8 @@ def test_library_exports_header_symbols():
     lib = binding.library()
     names = _declared_functions()
     assert names == ["attn_decode_fwd", "attn_decode_workspace_bytes", "attn_merge_partials",
-                     "attn_prefill_fwd", "attn_prefill_fwd_chunk", "attn_prefill_fwd_fp8",
-                     "attn_prefill_strerror", "attn_prefill_version"]
+                     "attn_prefill_bwd", "attn_prefill_fwd", "attn_prefill_fwd_chunk",
+                     "attn_prefill_fwd_fp8", "attn_prefill_strerror", "attn_prefill_version"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -191,3 +191,26 @@ def _call_fp8(**kw):
 ])
 def test_fp8_bad_arguments_rejected_on_host(kw, code):
     assert _call_fp8(**kw) == code
+
+
+def _call_bwd(**kw):
+    M = 0x10000000
+    args = dict(q=ALIGNED, k=ALIGNED + M, v=ALIGNED + 2 * M, out=ALIGNED + 3 * M,
+                lse=ALIGNED + 4 * M, dout=ALIGNED + 5 * M, dq=ALIGNED + 6 * M, dk=ALIGNED + 7 * M,
+                dv=ALIGNED + 8 * M, delta=ALIGNED + 9 * M, B=1, L=256, n_q=8, n_kv=2, d_h=128,
+                scale=0.088, causal=1, stream=0)
+    args.update(kw)
+    return binding.bwd_raw(*(args[n] for n in ("q", "k", "v", "out", "lse", "dout", "dq", "dk",
+                                               "dv", "delta", "B", "L", "n_q", "n_kv", "d_h",
+                                               "scale", "causal", "stream")))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dout=0), 1), (dict(delta=0), 1), (dict(L=0), 2), (dict(n_q=3), 3), (dict(d_h=64), 4),
+    (dict(scale=float("inf")), 5), (dict(causal=-1), 6),
+    (dict(dq=ALIGNED + 6 * 0x10000000 + 8), 7), (dict(delta=ALIGNED + 9 * 0x10000000 + 2), 7),
+    (dict(dk=ALIGNED + 0x10000000 + 256), 9), (dict(dv=ALIGNED + 7 * 0x10000000 + 4096), 9),
+    (dict(delta=ALIGNED + 4 * 0x10000000), 9),
+])
+def test_bwd_bad_arguments_rejected_on_host(kw, code):
+    assert _call_bwd(**kw) == code
