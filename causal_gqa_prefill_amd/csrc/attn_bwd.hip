@@ -14,9 +14,11 @@
 // Three kernels, no atomics:
 //  * bwd_delta_kernel: D for every row (HBM-bound).
 //  * bwd_dkdv_kernel: work item = (b, kv-head, 128-key block); four waves,
-//    32 keys each, stream 32-row tiles of Q and dO (and the rows' LSE and D)
-//    of every query head of the group through LDS and accumulate dK^T and
-//    dV^T in registers.  Per tile and wave: S = Q K^T and dP = dO V^T with
+//    32 keys each (their K rows in registers, the item's V rows in LDS),
+//    stream 32-row tiles of Q and dO (and the rows' LSE and D) of every query
+//    head of the group through LDS and accumulate dK^T and dV^T in
+//    registers; 65 KB of LDS and under 256 registers let two workgroups
+//    share a CU.  Per tile and wave: S = Q K^T and dP = dO V^T with
 //    queries as rows, so the accumulator holds one key per lane and 16
 //    queries in the slot order of the B operand; then dV^T += dO^T P and
 //    dK^T += Q^T dS with dO^T and Q^T read from LDS by the transpose read.
@@ -131,15 +133,16 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
   constexpr int ROWB = kBRowB;
   constexpr int KSTEPS = D / 16;
   constexpr int TBLK = D / 32;
-  constexpr int KV_BYTES = kKvKeys * ROWB;        // 32 KB: the item's K (or V) rows
+  constexpr int V_BYTES = kKvKeys * ROWB;         // 32 KB: the item's V rows
   constexpr int QT_BYTES = kQT * ROWB;            // 8 KB: one Q (or dO) tile
-  constexpr int KOFF = 0, VOFF = KV_BYTES;
-  constexpr int QOFF = 2 * KV_BYTES;              // 2 buffers of Q tiles
+  constexpr int VOFF = 0;
+  constexpr int QOFF = V_BYTES;                   // 2 buffers of Q tiles
   constexpr int DOOFF = QOFF + 2 * QT_BYTES;      // 2 buffers of dO tiles
   constexpr int STOFF = DOOFF + 2 * QT_BYTES;     // 2 buffers x (64 lse + 64 delta) floats
-  constexpr int SMEM = STOFF + 2 * 2 * 64 * 4;
-  constexpr int KV_LOADS = KV_BYTES / (kKvWaves * 1024);   // 8 per wave
+  constexpr int SMEM = STOFF + 2 * 2 * 64 * 4;    // 65 KB: two workgroups per CU
+  constexpr int V_LOADS = V_BYTES / (kKvWaves * 1024);     // 8 per wave
   constexpr int QT_LOADS = QT_BYTES / (kKvWaves * 1024);   // 2 per wave
+  static_assert(kKvWaves * 32 * ROWB <= SMEM, "output staging must fit");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
   LDS_AS unsigned char* const sl = (LDS_AS unsigned char*)smem;
 
@@ -159,18 +162,26 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
   const int k0 = kb * kKvKeys;
   const int kw0 = k0 + 32 * wave;                 // this wave's first key
 
-  const unsigned short* kbase = k + ((size_t)b * n_kv + kvh) * (size_t)L * D;
-  const unsigned short* vbase = v + ((size_t)b * n_kv + kvh) * (size_t)L * D;
-
-  // the item's K and V rows into LDS (rows past L read as zero)
+  // this wave's K rows as the B operand of S = Q K^T, straight from memory
+  // into registers (zero past L): key kw0 + col, elements 16 kk + 8 hi .. +8
+  bf16x8 kf[KSTEPS];
   {
-    int src[KV_LOADS];
+    const size_t kvrow = ((size_t)b * n_kv + kvh) * (size_t)L + (size_t)(kw0 + col);
 #pragma unroll
-    for (int s = 0; s < KV_LOADS; ++s) src[s] = tile_src<false>(wave * KV_LOADS, s, lane);
-    dma_tile(kbase, src, KV_LOADS, ROWB, k0, L, kKvKeys,
-             smem + KOFF + wave * KV_LOADS * 1024);
-    dma_tile(vbase, src, KV_LOADS, ROWB, k0, L, kKvKeys,
-             smem + VOFF + wave * KV_LOADS * 1024);
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if (kw0 + col < L) a = *reinterpret_cast<const u32x4*>(k + kvrow * D + kk * 16 + hi * 8);
+      kf[kk] = __builtin_bit_cast(bf16x8, a);
+    }
+  }
+  // the item's V rows into LDS (rows past L read as zero), the B operand of
+  // dP = dO V^T
+  {
+    int src[V_LOADS];
+#pragma unroll
+    for (int s = 0; s < V_LOADS; ++s) src[s] = tile_src<false>(wave * V_LOADS, s, lane);
+    dma_tile(v + ((size_t)b * n_kv + kvh) * (size_t)L * D, src, V_LOADS, ROWB, k0, L, kKvKeys,
+             smem + VOFF + wave * V_LOADS * 1024);
   }
   int qsrc[QT_LOADS];
 #pragma unroll
@@ -228,20 +239,19 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
     if (causal && q0 + kQT - 1 < kw0) continue;
     LDS_AS const unsigned char* qt = sl + QOFF + buf * QT_BYTES;
     LDS_AS const unsigned char* dot = sl + DOOFF + buf * QT_BYTES;
-    LDS_AS const unsigned char* kt = sl + KOFF + 32 * wave * ROWB;
     LDS_AS const unsigned char* vt = sl + VOFF + 32 * wave * ROWB;
     LDS_AS const float* st = (LDS_AS const float*)(sl + STOFF + buf * 512);
 
     // S = Q K^T and dP = dO V^T: rows = queries (A from the Q / dO tile),
-    // columns = this wave's keys (B from its K / V rows)
+    // columns = this wave's keys (B from its K / V registers)
     f32x16 S, dP;
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       const int ch = 2 * kk + hi;
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(qt, col, ch, swz_tr(col)),
-                                                 frag16(kt, col, ch, swz_row(col)), S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(qt, col, ch, swz_tr(col)), kf[kk], S, 0,
+                                                 0, 0);
       dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(dot, col, ch, swz_tr(col)),
                                                   frag16(vt, col, ch, swz_row(col)), dP, 0, 0,
                                                   0);
@@ -280,12 +290,12 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
   }
   wait_vmcnt<0>();
 
-  // ---- epilogue: dK = scale dK^T^T, dV = dV^T^T in bf16, staged through
-  // LDS as whole rows (the Q/dO buffers and K rows are free now)
+  // ---- epilogue: dK = scale dK^T^T, then dV = dV^T^T, in bf16, each staged
+  // through LDS (8 KB per wave) as whole rows
   tile_barrier();
-  LDS_AS unsigned char* ot = sl + wave * 2 * 32 * ROWB;   // 16 KB per wave: dK rows, dV rows
+  LDS_AS unsigned char* ot = sl + wave * 32 * ROWB;
 #pragma unroll
-  for (int which = 0; which < 2; ++which)
+  for (int which = 0; which < 2; ++which) {
 #pragma unroll
     for (int tb = 0; tb < TBLK; ++tb)
 #pragma unroll
@@ -295,23 +305,19 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
         for (int e = 0; e < 4; ++e)
           o4[e] = (__bf16)(which == 0 ? dkT[tb][grp * 4 + e] * scale : dvT[tb][grp * 4 + e]);
         const int chunk = tb * 4 + grp;
-        *reinterpret_cast<LDS_AS u32x2*>(ot + which * 32 * ROWB + col * ROWB +
-                                         ((chunk ^ swz_row(col)) << 4) + hi * 8) =
-            __builtin_bit_cast(u32x2, o4);
+        *reinterpret_cast<LDS_AS u32x2*>(ot + col * ROWB + ((chunk ^ swz_row(col)) << 4) +
+                                         hi * 8) = __builtin_bit_cast(u32x2, o4);
       }
-  // a wave reads back only the rows it wrote: no barrier needed
-#pragma unroll
-  for (int which = 0; which < 2; ++which) {
+    // a wave reads back only the rows it wrote, in order: no barrier needed
     unsigned short* gbase = (which == 0 ? dk : dv) + (((size_t)b * n_kv + kvh) * L + kw0) * D;
 #pragma unroll
     for (int st = 0; st < 32 * ROWB / 1024; ++st) {
       const int byte = st * 1024 + lane * 16;
       const int row = byte / ROWB;
       const int chunk = (byte % ROWB) >> 4;
-      const u32x4 v4 = *reinterpret_cast<const LDS_AS u32x4*>(
-          ot + which * 32 * ROWB + row * ROWB + ((chunk ^ swz_row(row)) << 4));
-      if (kw0 + row < L)
-        *reinterpret_cast<u32x4*>(gbase + (size_t)row * D + chunk * 8) = v4;
+      const u32x4 v4 =
+          *reinterpret_cast<const LDS_AS u32x4*>(ot + row * ROWB + ((chunk ^ swz_row(row)) << 4));
+      if (kw0 + row < L) *reinterpret_cast<u32x4*>(gbase + (size_t)row * D + chunk * 8) = v4;
     }
   }
 }
