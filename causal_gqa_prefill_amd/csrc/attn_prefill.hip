@@ -609,18 +609,20 @@ __global__ __launch_bounds__(256) void merge_kernel(
 // "Attention itself"; "Long-Context Attention Explained", the paragraphs on
 // prefill against decode).
 //
-// decode_split_kernel: work item = (b, kv-head, key range).  Four waves per
-// workgroup; wave w streams the 64-key tiles w, w + 4, ... of the range
-// through its own 32 KB of LDS (K tile, V tile) with the same DMA loads,
-// swizzles and fragment reads as the prefill kernel, and forms the g query
-// heads of the group as the 32 columns of S^T = K Q^T (columns >= g hold
-// zero queries and are never stored).  The four waves' running states merge
-// in LDS at the end, and the workgroup writes one fp32 partial per query
-// head: O normalised by the range's own row sum, and the range's LSE.
+// decode_split_kernel: work item = (b, kv-head, key range).  Eight waves per
+// workgroup, two per SIMD so that one computes while the other waits for
+// memory; wave w streams the 32-key tiles w, w + 8, ... of the range through
+// its own LDS (K tile, V tile) with the same DMA loads, swizzles and fragment
+// reads as the prefill kernel, and forms the g query heads of the group as
+// the 32 columns of S^T = K Q^T (columns >= g hold zero queries and are
+// never stored).  The waves' running states merge in LDS at the end, and the
+// workgroup writes one fp32 partial per query head: O normalised by the
+// range's own row sum, and the range's LSE.
 // decode_combine_kernel then merges the partials of each row by their LSEs
 // (the online-softmax combination, "Long-Context Attention Explained",
 // section "Online softmax").
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 8;
+constexpr int kDecTile = 32;          // keys per wave tile
 constexpr int kDecMaxSplits = 4096;   // partials per row the combine stages in LDS
 
 template <int D>
@@ -631,12 +633,13 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
   constexpr int KSTEPS = D / 16;
   constexpr int TBLK = D / 32;
   constexpr int ROWB = 2 * D;
-  constexpr int TILE = kBC * ROWB;           // bytes of one 64-key K or V tile
+  constexpr int TILE = kDecTile * ROWB;      // bytes of one 32-key K or V tile
   constexpr int LOADS = TILE / 1024;         // 1 KB loads per tile, one wave
   constexpr int WAVE_LDS = 2 * TILE;         // a wave's K tile then its V tile
-  static_assert(32 * D * 4 + 2 * 32 * 4 <= WAVE_LDS, "wave state must fit its LDS");
+  static_assert(32 * D * 4 <= WAVE_LDS, "a wave's accumulators must fit its LDS");
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kDecWaves * WAVE_LDS];
+  __shared__ float st_ml[kDecWaves][64];     // each wave's m[32] and l[32]
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -705,15 +708,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
   float l_run = 0.0f;        // this lane's part of the row sum
   const float c2 = scale * kLog2e;
 
-  for (int t0 = j_begin + wave * kBC; t0 < j_end; t0 += kDecWaves * kBC) {
+  for (int t0 = j_begin + wave * kDecTile; t0 < j_end; t0 += kDecWaves * kDecTile) {
     wait_lgkm0();   // the previous tile's LDS reads are done before it is overwritten
-    dma_tile(kbase, k_src, LOADS, ROWB, t0, j_end, kBC, wbuf);
-    dma_tile(vbase, v_src, LOADS, ROWB, t0, j_end, kBC, wbuf + TILE);
+    dma_tile(kbase, k_src, LOADS, ROWB, t0, j_end, kDecTile, wbuf);
+    dma_tile(vbase, v_src, LOADS, ROWB, t0, j_end, kDecTile, wbuf + TILE);
     wait_vmcnt<0>();
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      const int j0 = t0 + 32 * jb;
-      if (j0 >= j_end) break;
+    {
+      constexpr int jb = 0;
+      const int j0 = t0;
       bf16x8 kf[KSTEPS];
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk)
@@ -767,16 +769,15 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
     }
   }
 
-  // ---- merge the four waves' states in LDS: wave w leaves m[32], l[32]
-  // and its unnormalised O as [32 columns][D] fp32 in its own LDS
+  // ---- merge the waves' states in LDS: wave w leaves m[32], l[32] in
+  // st_ml[w] and its unnormalised O as [32 columns][D] fp32 in its own LDS
   const float l_tot = pair_sum(l_run);
   __syncthreads();   // every wave is past its last LDS read and tile load
   {
-    float* st = reinterpret_cast<float*>(wbuf);
-    float* acc_out = st + 64;
+    float* acc_out = reinterpret_cast<float*>(wbuf);
     if (hi == 0) {
-      st[col] = m_run;
-      st[32 + col] = l_tot;
+      st_ml[wave][col] = m_run;
+      st_ml[wave][32 + col] = l_tot;
     }
 #pragma unroll
     for (int tb = 0; tb < TBLK; ++tb)
@@ -799,17 +800,17 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
     float m_all = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) {
-      mw[w] = reinterpret_cast<const float*>(smem + w * WAVE_LDS)[c];
+      mw[w] = st_ml[w][c];
       m_all = fmaxf(m_all, mw[w]);
     }
     float num = 0.0f, den = 0.0f;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) {
-      const float* st = reinterpret_cast<const float*>(smem + w * WAVE_LDS);
+      const float* acc_w = reinterpret_cast<const float*>(smem + w * WAVE_LDS);
       // a wave without a tile has m = -inf, l = 0 and O = 0: weight 0
       const float f = __builtin_amdgcn_exp2f(mw[w] - m_all);
-      den += f * st[32 + c];
-      num += f * st[64 + c * D + d];
+      den += f * st_ml[w][32 + c];
+      num += f * acc_w[c * D + d];
     }
     const size_t prow = ((size_t)b * n_q + (size_t)kvh * g + c) * n_split + split;
     ws_o[prow * D + d] = num / den;
@@ -894,28 +895,37 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   }
 }
 
-// Key ranges of a decode call: enough work items to give every CU several
-// (a multiple of 256 keys per range, so each of the four waves gets whole
-// tiles), and never more than kDecMaxSplits ranges per row.
+// Key ranges of a decode call.  One workgroup fills a CU (its LDS), so the
+// workgroups run in rounds of 256 and a call takes about (rounds) x (keys per
+// range).  Ranges are multiples of 256 keys (each of the eight waves gets
+// whole 32-key tiles); the count per row is chosen to minimise that product,
+// preferring fewer ranges (less to combine), and never exceeds
+// kDecMaxSplits.
 struct DecodeSplit {
   int n_split, split_keys;
 };
 DecodeSplit decode_split(int B, int Lk, int n_kv) {
+  constexpr long long kCUs = 256;
   const long long pairs = (long long)B * n_kv;
-  const long long target = 1024;   // about four workgroups per CU
-  long long want = (target + pairs - 1) / pairs;
-  const long long max_by_keys = ((long long)Lk + 255) / 256;
-  if (want > max_by_keys) want = max_by_keys;
-  if (want < 1) want = 1;
-  long long per = ((long long)Lk + want - 1) / want;
-  per = (per + 255) / 256 * 256;
-  long long n = ((long long)Lk + per - 1) / per;
-  if (n > kDecMaxSplits) {
-    per = ((long long)Lk + kDecMaxSplits - 1) / kDecMaxSplits;
-    per = (per + 255) / 256 * 256;
-    n = ((long long)Lk + per - 1) / per;
+  const long long chunks = ((long long)Lk + 255) / 256;   // 256-key pieces
+  const long long max_n = chunks < kDecMaxSplits ? chunks : kDecMaxSplits;
+  long long best_n = 1, best_per = chunks * 256, best_cost = -1;
+  // visit each distinct range length once: q = ceil(chunks / n) 256-key pieces
+  for (long long n = 1; n <= max_n;) {
+    const long long q = (chunks + n - 1) / n;
+    const long long per = q * 256;                                // keys per range
+    const long long n_act = ((long long)Lk + per - 1) / per;      // ranges actually used
+    const long long rounds = (pairs * n_act + kCUs - 1) / kCUs;
+    const long long cost = rounds * per * 64 + n_act;             // keys x rounds, then fewer ranges
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_n = n_act;
+      best_per = per;
+    }
+    if (q == 1) break;
+    n = (chunks + q - 2) / (q - 1);   // the first n with fewer pieces per range
   }
-  return DecodeSplit{(int)n, (int)per};
+  return DecodeSplit{(int)best_n, (int)best_per};
 }
 
 }  // namespace
