@@ -128,7 +128,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
     const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
     unsigned short* __restrict__ dk, unsigned short* __restrict__ dv, int L, int n_q, int n_kv,
-    int n_kblk, float scale, int causal) {
+    int n_kblk, int mirror, float scale, int causal) {
   constexpr int D = kBD;
   constexpr int ROWB = kBRowB;
   constexpr int KSTEPS = D / 16;
@@ -152,9 +152,13 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
   const int hi = lane >> 5;
   const int col = lane & 31;
 
-  // work item: key blocks in order (block 0, the one most queries see, first)
+  // work item: key blocks in order (block 0, the one most queries see,
+  // first).  When the whole grid runs at once (mirror), the second half of
+  // the blocks comes in reverse, so that the two workgroups sharing a CU
+  // (items i and i + half) take blocks k and n - 1 - k: equal causal work.
   const int item = blockIdx.x;
-  const int kb = item / (gridDim.x / n_kblk);
+  const int pos = item / (gridDim.x / n_kblk);
+  const int kb = (mirror && pos >= (n_kblk + 1) / 2) ? n_kblk - 1 - (pos - (n_kblk + 1) / 2) : pos;
   const int rest = item % (gridDim.x / n_kblk);
   const int kvh = rest % n_kv;
   const int b = rest / n_kv;
@@ -557,12 +561,15 @@ extern "C" int attn_prefill_bwd(const void* q, const void* k, const void* v, con
                      static_cast<const unsigned short*>(out),
                      static_cast<const unsigned short*>(dout), delta, (long long)rows);
   if (hipGetLastError() != hipSuccess) return ATTN_PREFILL_ERR_LAUNCH;
+  // one round of the whole grid (two workgroups on each of the 256 CUs):
+  // pair heavy and light key blocks on each CU
+  const int mirror = causal && kv_grid <= 2 * 256;
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_grid), dim3(64 * kKvWaves), 0, stream,
                      static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
                      static_cast<const unsigned short*>(v),
                      static_cast<const unsigned short*>(dout), lse, delta,
                      static_cast<unsigned short*>(dk), static_cast<unsigned short*>(dv), L, n_q,
-                     n_kv, (int)n_kblk, scale, causal);
+                     n_kv, (int)n_kblk, mirror, scale, causal);
   if (hipGetLastError() != hipSuccess) return ATTN_PREFILL_ERR_LAUNCH;
   switch (bwd_pick_hwg(n_q / n_kv)) {
     case 8: return launch_dq<8>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);
