@@ -609,10 +609,10 @@ __global__ __launch_bounds__(256) void merge_kernel(
 // "Attention itself"; "Long-Context Attention Explained", the paragraphs on
 // prefill against decode).
 //
-// decode_split_kernel: work item = (b, kv-head, key range).  Eight waves per
-// workgroup, two per SIMD so that one computes while the other waits for
-// memory; wave w streams the 32-key tiles w, w + 8, ... of the range through
-// its own LDS (K tile, V tile) with the same DMA loads, swizzles and fragment
+// decode_split_kernel: work item = (b, kv-head, key range).  Four waves per
+// workgroup and two workgroups per CU (65 KB of LDS each), two waves per SIMD
+// so that one computes while the other waits for memory; wave w streams the
+// 32-key tiles w, w + 4, ... of the range through its own LDS (K tile, V tile) with the same DMA loads, swizzles and fragment
 // reads as the prefill kernel, and forms the g query heads of the group as
 // the 32 columns of S^T = K Q^T (columns >= g hold zero queries and are
 // never stored).  The waves' running states merge in LDS at the end, and the
@@ -621,8 +621,9 @@ __global__ __launch_bounds__(256) void merge_kernel(
 // decode_combine_kernel then merges the partials of each row by their LSEs
 // (the online-softmax combination, "Long-Context Attention Explained",
 // section "Online softmax").
-constexpr int kDecWaves = 8;
+constexpr int kDecWaves = 4;
 constexpr int kDecTile = 32;          // keys per wave tile
+constexpr int kDecSlots = 512;        // workgroups resident at once (two per CU)
 constexpr int kDecMaxSplits = 4096;   // partials per row the combine stages in LDS
 
 template <int D>
@@ -895,9 +896,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   }
 }
 
-// Key ranges of a decode call.  One workgroup fills a CU (its LDS), so the
-// workgroups run in rounds of 256 and a call takes about (rounds) x (keys per
-// range).  Ranges are multiples of 256 keys (each of the eight waves gets
+// Key ranges of a decode call.  Two workgroups fill a CU (their LDS), so the
+// workgroups run in rounds of 512 and a call takes about (rounds) x (keys per
+// range + a fixed cost per workgroup).  Ranges are multiples of 256 keys (each of the four waves gets
 // whole 32-key tiles); the count per row is chosen to minimise that product,
 // preferring fewer ranges (less to combine), and never exceeds
 // kDecMaxSplits.
@@ -905,7 +906,6 @@ struct DecodeSplit {
   int n_split, split_keys;
 };
 DecodeSplit decode_split(int B, int Lk, int n_kv) {
-  constexpr long long kCUs = 256;
   const long long pairs = (long long)B * n_kv;
   const long long chunks = ((long long)Lk + 255) / 256;   // 256-key pieces
   const long long max_n = chunks < kDecMaxSplits ? chunks : kDecMaxSplits;
@@ -915,8 +915,10 @@ DecodeSplit decode_split(int B, int Lk, int n_kv) {
     const long long q = (chunks + n - 1) / n;
     const long long per = q * 256;                                // keys per range
     const long long n_act = ((long long)Lk + per - 1) / per;      // ranges actually used
-    const long long rounds = (pairs * n_act + kCUs - 1) / kCUs;
-    const long long cost = rounds * per * 64 + n_act;             // keys x rounds, then fewer ranges
+    const long long rounds = (pairs * n_act + kDecSlots - 1) / kDecSlots;
+    // keys x rounds, with each workgroup's start and merge costing about
+    // 256 keys' worth of streaming; then fewer ranges
+    const long long cost = rounds * (per + 256) * 64 + n_act;
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
       best_n = n_act;
