@@ -41,20 +41,26 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBD = 128;          // head size
-constexpr int kBRowB = 2 * kBD;   // bytes per bf16 row
-
-// 16-byte chunk swizzles of 256-byte rows: "row" for tiles read by 16-byte
-// row reads (16 lanes take 16 consecutive rows at one chunk), "tr" for tiles
-// read by the transpose read (32 lanes take 4 rows x 2 chunk pairs).
-__device__ __forceinline__ int swz_row(int row) { return row & 15; }
-__device__ __forceinline__ int swz_tr(int row) { return (row & 3) << 2; }
+// 16-byte chunk swizzles of rows of 2 D bytes: "row" for tiles read by
+// 16-byte row reads (16 lanes take 16 consecutive rows at one chunk), "tr"
+// for tiles read by the transpose read (32 lanes take 4 rows x 2 chunk
+// pairs); the same spreads over the banks as the forward kernel's K and V
+// swizzles (for D = 64 two rows share a 256-byte window).
+template <int D>
+__device__ __forceinline__ int swz_row(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_tr(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
 
 // A 16-byte operand fragment of row `row` (relative to a tile at `base`),
 // logical chunk `chunk`, under swizzle `swz`.
+template <int D>
 __device__ __forceinline__ bf16x8 frag16(LDS_AS const unsigned char* base, int row, int chunk,
                                          int swz) {
-  return *reinterpret_cast<const LDS_AS bf16x8*>(base + row * kBRowB + ((chunk ^ swz) << 4));
+  return *reinterpret_cast<const LDS_AS bf16x8*>(base + row * (2 * D) + ((chunk ^ swz) << 4));
 }
 
 // Transposed operand: for lanes l (hi = l / 32) of a 32-row block at `base`
@@ -62,8 +68,10 @@ __device__ __forceinline__ bf16x8 frag16(LDS_AS const unsigned char* base, int r
 // 4 hi + s % 4), the 8 values of column 32 tb + l % 32 for k-step ks.
 // In each group of 16 lanes, lane 4 r + qq supplies four consecutive 16-bit
 // values of row r and lane i receives column i of the four rows.
+template <int D>
 __device__ __forceinline__ bf16x8 frag_tr(LDS_AS const unsigned char* base, int tb, int ks,
                                           int lane) {
+  constexpr int ROWB = 2 * D;
   const int hi = lane >> 5;
   const int tr_r = (lane >> 2) & 3;
   const int tr_q = lane & 3;
@@ -71,9 +79,9 @@ __device__ __forceinline__ bf16x8 frag_tr(LDS_AS const unsigned char* base, int 
   const int t = 32 * tb + 16 * tr_g + 4 * tr_q;
   const int key = 16 * ks + 4 * hi + tr_r;
   const LDS_AS unsigned char* p =
-      base + key * kBRowB + (((t >> 3) ^ swz_tr(key)) << 4) + ((t >> 2) & 1) * 8;
+      base + key * ROWB + (((t >> 3) ^ swz_tr<D>(key)) << 4) + ((t >> 2) & 1) * 8;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
-  const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 8 * kBRowB));
+  const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 8 * ROWB));
   return __builtin_bit_cast(
       bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                       __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]});
@@ -82,26 +90,29 @@ __device__ __forceinline__ bf16x8 frag_tr(LDS_AS const unsigned char* base, int 
 // Source offsets of one wave's share of a tile load (rows of 256 bytes,
 // `loads` loads of 1 KB starting at LDS byte 1 KB * first), placing logical
 // chunk c of row r at physical chunk c ^ swz(r).
-template <bool TR>
+template <int D, bool TR>
 __device__ __forceinline__ int tile_src(int first, int s, int lane) {
+  constexpr int ROWB = 2 * D;
   const int byte = (first + s) * 1024 + lane * 16;
-  const int row = byte / kBRowB;
-  const int pos = (byte % kBRowB) >> 4;
-  return row * kBRowB + ((pos ^ (TR ? swz_tr(row) : swz_row(row))) << 4);
+  const int row = byte / ROWB;
+  const int pos = (byte % ROWB) >> 4;
+  return row * ROWB + ((pos ^ (TR ? swz_tr<D>(row) : swz_row<D>(row))) << 4);
 }
 
-// ---- D_i = dO_i . O_i, fp32: 16 lanes per row (8 elements each)
+// ---- D_i = dO_i . O_i, fp32: D / 8 lanes per row (8 elements each)
+template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const unsigned short* __restrict__ out,
                                                         const unsigned short* __restrict__ dout,
                                                         float* __restrict__ delta,
                                                         long long rows) {
+  constexpr int PER_ROW = D / 8;
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = gid >> 4;
-  const int part = threadIdx.x & 15;
+  const long long row = gid / PER_ROW;
+  const int part = threadIdx.x % PER_ROW;
   float acc = 0.0f;
   if (row < rows) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(out + row * kBD + part * 8);
-    const u32x4 d = *reinterpret_cast<const u32x4*>(dout + row * kBD + part * 8);
+    const u32x4 a = *reinterpret_cast<const u32x4*>(out + row * D + part * 8);
+    const u32x4 d = *reinterpret_cast<const u32x4*>(dout + row * D + part * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       // copy the element out first: a bit cast of an ext-vector element
@@ -114,7 +125,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const unsigned short* __
     }
   }
 #pragma unroll
-  for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 16);
+  for (int o = PER_ROW / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, PER_ROW);
   if (row < rows && part == 0) delta[row] = acc;
 }
 
@@ -123,14 +134,14 @@ constexpr int kKvWaves = 4;                    // 32 keys per wave
 constexpr int kKvKeys = 32 * kKvWaves;         // keys per work item
 constexpr int kQT = 32;                        // query rows per tile
 
+template <int D>
 __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
     unsigned short* __restrict__ dk, unsigned short* __restrict__ dv, int L, int n_q, int n_kv,
     int n_kblk, int mirror, float scale, int causal) {
-  constexpr int D = kBD;
-  constexpr int ROWB = kBRowB;
+  constexpr int ROWB = 2 * D;
   constexpr int KSTEPS = D / 16;
   constexpr int TBLK = D / 32;
   constexpr int V_BYTES = kKvKeys * ROWB;         // 32 KB: the item's V rows
@@ -183,29 +194,30 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
   {
     int src[V_LOADS];
 #pragma unroll
-    for (int s = 0; s < V_LOADS; ++s) src[s] = tile_src<false>(wave * V_LOADS, s, lane);
+    for (int s = 0; s < V_LOADS; ++s) src[s] = tile_src<D, false>(wave * V_LOADS, s, lane);
     dma_tile(v + ((size_t)b * n_kv + kvh) * (size_t)L * D, src, V_LOADS, ROWB, k0, L, kKvKeys,
              smem + VOFF + wave * V_LOADS * 1024);
   }
   int qsrc[QT_LOADS];
 #pragma unroll
-  for (int s = 0; s < QT_LOADS; ++s) qsrc[s] = tile_src<true>(wave * QT_LOADS, s, lane);
+  for (int s = 0; s < QT_LOADS; ++s) qsrc[s] = tile_src<D, true>(wave * QT_LOADS, s, lane);
 
   // query tiles: every head of the group, rows from the first tile that can
   // see a key of the block (causal) or from 0
   const int qt_first = causal ? k0 / kQT : 0;
   const int qt_per_head = (L + kQT - 1) / kQT - qt_first;
   const int n_qt = g * qt_per_head;
-  auto tile_rows = [&] __device__ (int n, int& h, int& q0) __attribute__((always_inline)) {
-    h = kvh * g + n / qt_per_head;
-    q0 = (qt_first + n % qt_per_head) * kQT;
+  auto tile_head = [&] __device__ (int n) __attribute__((always_inline)) {
+    return kvh * g + n / qt_per_head;
+  };
+  auto tile_q0 = [&] __device__ (int n) __attribute__((always_inline)) {
+    return (qt_first + n % qt_per_head) * kQT;
   };
   // loads of tile n into buffer n % 2: Q and dO rows (zero past L), and the
   // rows' LSE and delta (wave 0, 4 bytes per lane; zero past L)
   auto load_qtile = [&] __device__ (int n) __attribute__((always_inline)) {
-    int h, q0;
-    tile_rows(n, h, q0);
-    const size_t rowbase = ((size_t)b * n_q + h) * (size_t)L;
+    const int q0 = tile_q0(n);
+    const size_t rowbase = ((size_t)b * n_q + tile_head(n)) * (size_t)L;
     const int buf = n & 1;
     dma_tile(q + rowbase * D, qsrc, QT_LOADS, ROWB, q0, L, kQT,
              smem + QOFF + buf * QT_BYTES + wave * QT_LOADS * 1024);
@@ -235,9 +247,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
     wait_vmcnt<0>();
     tile_barrier();
     if (n + 1 < n_qt) load_qtile(n + 1);
-    int h, q0;
-    tile_rows(n, h, q0);
-    (void)h;
+    const int q0 = tile_q0(n);
     const int buf = n & 1;
     // skip when every query of the tile is before every key of the wave
     if (causal && q0 + kQT - 1 < kw0) continue;
@@ -254,10 +264,10 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       const int ch = 2 * kk + hi;
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(qt, col, ch, swz_tr(col)), kf[kk], S, 0,
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16<D>(qt, col, ch, swz_tr<D>(col)), kf[kk], S, 0,
                                                  0, 0);
-      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(dot, col, ch, swz_tr(col)),
-                                                  frag16(vt, col, ch, swz_row(col)), dP, 0, 0,
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16<D>(dot, col, ch, swz_tr<D>(col)),
+                                                  frag16<D>(vt, col, ch, swz_row<D>(col)), dP, 0, 0,
                                                   0);
     }
     // P = 2^(c2 s - log2e lse), dS = P (dP - D); lane (key col) holds
@@ -286,9 +296,9 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int tb = 0; tb < TBLK; ++tb) {
-        dvT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(dot, tb, ks, lane), pk[ks],
+        dvT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(dot, tb, ks, lane), pk[ks],
                                                          dvT[tb], 0, 0, 0);
-        dkT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(qt, tb, ks, lane), dsk[ks],
+        dkT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(qt, tb, ks, lane), dsk[ks],
                                                          dkT[tb], 0, 0, 0);
       }
   }
@@ -309,7 +319,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
         for (int e = 0; e < 4; ++e)
           o4[e] = (__bf16)(which == 0 ? dkT[tb][grp * 4 + e] * scale : dvT[tb][grp * 4 + e]);
         const int chunk = tb * 4 + grp;
-        *reinterpret_cast<LDS_AS u32x2*>(ot + col * ROWB + ((chunk ^ swz_row(col)) << 4) +
+        *reinterpret_cast<LDS_AS u32x2*>(ot + col * ROWB + ((chunk ^ swz_row<D>(col)) << 4) +
                                          hi * 8) = __builtin_bit_cast(u32x2, o4);
       }
     // a wave reads back only the rows it wrote, in order: no barrier needed
@@ -320,7 +330,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
       const int row = byte / ROWB;
       const int chunk = (byte % ROWB) >> 4;
       const u32x4 v4 =
-          *reinterpret_cast<const LDS_AS u32x4*>(ot + row * ROWB + ((chunk ^ swz_row(row)) << 4));
+          *reinterpret_cast<const LDS_AS u32x4*>(ot + row * ROWB + ((chunk ^ swz_row<D>(row)) << 4));
       if (kw0 + row < L) *reinterpret_cast<u32x4*>(gbase + (size_t)row * D + chunk * 8) = v4;
     }
   }
@@ -331,15 +341,14 @@ constexpr int kDqCols = 256;   // query columns per workgroup (8 waves x 32)
 constexpr int kDqWaves = 8;
 constexpr int kDqKeys = 64;    // keys per K/V tile
 
-template <int HWG>
+template <int D, int HWG>
 __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
     unsigned short* __restrict__ dq, int L, int n_q, int n_kv, int n_qblk, int items_per_qblk,
     float scale, int causal) {
-  constexpr int D = kBD;
-  constexpr int ROWB = kBRowB;
+  constexpr int ROWB = 2 * D;
   constexpr int KSTEPS = D / 16;
   constexpr int TBLK = D / 32;
   constexpr int BR = kDqCols / HWG;
@@ -396,8 +405,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
   int ksrc[LOADS], vsrc[LOADS];
 #pragma unroll
   for (int s = 0; s < LOADS; ++s) {
-    ksrc[s] = tile_src<true>(wave * LOADS, s, lane);    // K: row reads and transpose reads
-    vsrc[s] = tile_src<false>(wave * LOADS, s, lane);   // V: row reads
+    ksrc[s] = tile_src<D, true>(wave * LOADS, s, lane);    // K: row reads and transpose reads
+    vsrc[s] = tile_src<D, false>(wave * LOADS, s, lane);   // V: row reads
   }
   auto load_tiles = [&] __device__ (int t) __attribute__((always_inline)) {
     const int buf = t & 1;
@@ -435,9 +444,9 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         const int ch = 2 * kk + hi;
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(kh, col, ch, swz_tr(col)), qf[kk], S,
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16<D>(kh, col, ch, swz_tr<D>(col)), qf[kk], S,
                                                    0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(vh, col, ch, swz_row(col)), of[kk],
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16<D>(vh, col, ch, swz_row<D>(col)), of[kk],
                                                     dP, 0, 0, 0);
       }
       // dS^T = P^T (dP^T - D), lane (query col) holds keys 8 (r / 4) + 4 hi + r % 4
@@ -454,7 +463,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int tb = 0; tb < TBLK; ++tb)
-          dqT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(kh, tb, ks, lane), dsk[ks],
+          dqT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(kh, tb, ks, lane), dsk[ks],
                                                            dqT[tb], 0, 0, 0);
     }
   }
@@ -471,7 +480,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(dqT[tb][grp * 4 + e] * scale);
       const int chunk = tb * 4 + grp;
-      *reinterpret_cast<LDS_AS u32x2*>(ot + col * ROWB + ((chunk ^ swz_row(col)) << 4) +
+      *reinterpret_cast<LDS_AS u32x2*>(ot + col * ROWB + ((chunk ^ swz_row<D>(col)) << 4) +
                                        hi * 8) = __builtin_bit_cast(u32x2, o4);
     }
   unsigned short* obase = dq + (rowbase + q0) * D;
@@ -481,7 +490,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
     const int row = byte / ROWB;
     const int chunk = (byte % ROWB) >> 4;
     const u32x4 v4 =
-        *reinterpret_cast<const LDS_AS u32x4*>(ot + row * ROWB + ((chunk ^ swz_row(row)) << 4));
+        *reinterpret_cast<const LDS_AS u32x4*>(ot + row * ROWB + ((chunk ^ swz_row<D>(row)) << 4));
     if (q0 + row < L) *reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8) = v4;
   }
 }
@@ -493,7 +502,7 @@ int bwd_pick_hwg(int g) {
   return 1;
 }
 
-template <int HWG>
+template <int D, int HWG>
 int launch_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
               const float* delta, void* dq, int B, int L, int n_q, int n_kv, float scale,
               int causal, hipStream_t stream) {
@@ -502,13 +511,44 @@ int launch_dq(const void* q, const void* k, const void* v, const void* dout, con
   const long long items_per_qblk = (long long)B * n_kv * ((n_q / n_kv) / HWG);
   const long long grid = items_per_qblk * n_qblk;
   if (items_per_qblk > INT_MAX || grid > INT_MAX) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
-  hipLaunchKernelGGL((bwd_dq_kernel<HWG>), dim3((unsigned)grid), dim3(64 * kDqWaves), 0, stream,
-                     static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
-                     static_cast<const unsigned short*>(v),
+  hipLaunchKernelGGL((bwd_dq_kernel<D, HWG>), dim3((unsigned)grid), dim3(64 * kDqWaves), 0,
+                     stream, static_cast<const unsigned short*>(q),
+                     static_cast<const unsigned short*>(k), static_cast<const unsigned short*>(v),
                      static_cast<const unsigned short*>(dout), lse, delta,
                      static_cast<unsigned short*>(dq), L, n_q, n_kv, n_qblk,
                      (int)items_per_qblk, scale, causal);
   return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
+}
+
+// The three kernels of one backward call for head size D.
+template <int D>
+int launch_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int L,
+               int n_q, int n_kv, long long rows, float scale, int causal, hipStream_t stream) {
+  const long long n_kblk = ((long long)L + kKvKeys - 1) / kKvKeys;
+  const long long kv_grid = (long long)B * n_kv * n_kblk;
+  const long long delta_blocks = (rows * (D / 8) + 255) / 256;
+  if (kv_grid > INT_MAX || delta_blocks > INT_MAX) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)delta_blocks), dim3(256), 0, stream,
+                     static_cast<const unsigned short*>(out),
+                     static_cast<const unsigned short*>(dout), delta, rows);
+  if (hipGetLastError() != hipSuccess) return ATTN_PREFILL_ERR_LAUNCH;
+  // one round of the whole grid (two workgroups on each of the 256 CUs):
+  // pair heavy and light key blocks on each CU
+  const int mirror = causal && kv_grid <= 2 * 256;
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)kv_grid), dim3(64 * kKvWaves), 0, stream,
+                     static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
+                     static_cast<const unsigned short*>(v),
+                     static_cast<const unsigned short*>(dout), lse, delta,
+                     static_cast<unsigned short*>(dk), static_cast<unsigned short*>(dv), L, n_q,
+                     n_kv, (int)n_kblk, mirror, scale, causal);
+  if (hipGetLastError() != hipSuccess) return ATTN_PREFILL_ERR_LAUNCH;
+  switch (bwd_pick_hwg(n_q / n_kv)) {
+    case 8: return launch_dq<D, 8>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);
+    case 4: return launch_dq<D, 4>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);
+    case 2: return launch_dq<D, 2>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);
+    default: return launch_dq<D, 1>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);
+  }
 }
 
 }  // namespace
@@ -521,7 +561,7 @@ extern "C" int attn_prefill_bwd(const void* q, const void* k, const void* v, con
     return ATTN_PREFILL_ERR_NULL_PTR;
   if (B < 1 || L < 1 || n_q < 1 || n_kv < 1) return ATTN_PREFILL_ERR_BAD_SHAPE;
   if (n_q % n_kv != 0) return ATTN_PREFILL_ERR_BAD_GQA;
-  if (d_h != kBD) return ATTN_PREFILL_ERR_BAD_HEADDIM;
+  if (d_h != 64 && d_h != 128) return ATTN_PREFILL_ERR_BAD_HEADDIM;
   if (!std::isfinite(scale)) return ATTN_PREFILL_ERR_BAD_SCALE;
   if (causal != 0 && causal != 1) return ATTN_PREFILL_ERR_BAD_CAUSAL;
   const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
@@ -552,29 +592,9 @@ extern "C" int attn_prefill_bwd(const void* q, const void* k, const void* v, con
     for (int c = a + 1; c < 4; ++c)
       if (overlaps(outs[a], osz[a], outs[c], osz[c])) return ATTN_PREFILL_ERR_ALIASING;
   }
-  const long long n_kblk = ((long long)L + kKvKeys - 1) / kKvKeys;
-  const long long kv_grid = (long long)B * n_kv * n_kblk;
-  const long long delta_blocks = ((long long)rows * 16 + 255) / 256;
-  if (kv_grid > INT_MAX || delta_blocks > INT_MAX) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
-
-  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)delta_blocks), dim3(256), 0, stream,
-                     static_cast<const unsigned short*>(out),
-                     static_cast<const unsigned short*>(dout), delta, (long long)rows);
-  if (hipGetLastError() != hipSuccess) return ATTN_PREFILL_ERR_LAUNCH;
-  // one round of the whole grid (two workgroups on each of the 256 CUs):
-  // pair heavy and light key blocks on each CU
-  const int mirror = causal && kv_grid <= 2 * 256;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_grid), dim3(64 * kKvWaves), 0, stream,
-                     static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
-                     static_cast<const unsigned short*>(v),
-                     static_cast<const unsigned short*>(dout), lse, delta,
-                     static_cast<unsigned short*>(dk), static_cast<unsigned short*>(dv), L, n_q,
-                     n_kv, (int)n_kblk, mirror, scale, causal);
-  if (hipGetLastError() != hipSuccess) return ATTN_PREFILL_ERR_LAUNCH;
-  switch (bwd_pick_hwg(n_q / n_kv)) {
-    case 8: return launch_dq<8>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);
-    case 4: return launch_dq<4>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);
-    case 2: return launch_dq<2>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);
-    default: return launch_dq<1>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);
-  }
+  if (d_h == 128)
+    return launch_bwd<128>(q, k, v, out, lse, dout, dq, dk, dv, delta, B, L, n_q, n_kv,
+                           (long long)rows, scale, causal, stream);
+  return launch_bwd<64>(q, k, v, out, lse, dout, dq, dk, dv, delta, B, L, n_q, n_kv,
+                        (long long)rows, scale, causal, stream);
 }

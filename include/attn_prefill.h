@@ -182,12 +182,11 @@ int attn_prefill_fwd_fp8(const void *q, const void *k, const void *v, void *out,
  *   dq           : device pointer, bf16 [B, n_q, L, d_h], written entirely
  *   dk, dv       : device pointers, bf16 [B, n_kv, L, d_h], written entirely
  *   delta        : device pointer, fp32 [B, n_q, L], written (delta_i)
- *   d_h must be 128; other arguments as attn_prefill_fwd.
+ *   d_h in {64, 128}; other arguments as attn_prefill_fwd.
  * Numerics: P is recomputed in fp32 from lse, delta from the bf16 out; P and
  * dS are rounded to bf16 (nearest even) for the matrix-core products, which
  * accumulate in fp32; the gradients are rounded to bf16 once.  The outputs
- * may not overlap each other or any input.  Errors as for attn_prefill_fwd
- * (ATTN_PREFILL_ERR_BAD_HEADDIM for d_h != 128).
+ * may not overlap each other or any input.  Errors as for attn_prefill_fwd.
  */
 int attn_prefill_bwd(const void *q, const void *k, const void *v, const void *out,
                      const float *lse, const void *dout, void *dq, void *dk, void *dv,

@@ -206,7 +206,7 @@ def _call_bwd(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dout=0), 1), (dict(delta=0), 1), (dict(L=0), 2), (dict(n_q=3), 3), (dict(d_h=64), 4),
+    (dict(dout=0), 1), (dict(delta=0), 1), (dict(L=0), 2), (dict(n_q=3), 3), (dict(d_h=96), 4),
     (dict(scale=float("inf")), 5), (dict(causal=-1), 6),
     (dict(dq=ALIGNED + 6 * 0x10000000 + 8), 7), (dict(delta=ALIGNED + 9 * 0x10000000 + 2), 7),
     (dict(dk=ALIGNED + 0x10000000 + 256), 9), (dict(dv=ALIGNED + 7 * 0x10000000 + 4096), 9),

@@ -76,21 +76,25 @@ def _run_case(B, L, n_q, n_kv, d, causal, seed, q_rows=None, k_rows=None, label=
 
 
 SHAPES = [
-    # B, L, n_q, n_kv, causal
-    (1, 1, 4, 4, 1),
-    (1, 31, 4, 2, 1),
-    (1, 64, 8, 2, 1),
-    (2, 129, 6, 3, 1),
-    (1, 130, 4, 4, 0),
-    (1, 257, 8, 1, 1),
-    (1, 300, 16, 2, 0),
-    (1, 1000, 4, 2, 1),
+    # B, L, n_q, n_kv, d, causal
+    (1, 1, 4, 4, 128, 1),
+    (1, 31, 4, 2, 128, 1),
+    (1, 64, 8, 2, 128, 1),
+    (2, 129, 6, 3, 128, 1),
+    (1, 130, 4, 4, 128, 0),
+    (1, 257, 8, 1, 128, 1),
+    (1, 300, 16, 2, 128, 0),
+    (1, 1000, 4, 2, 128, 1),
+    (1, 1, 2, 1, 64, 1),
+    (1, 128, 4, 4, 64, 1),      # the tiny causal MHA workload's shape
+    (2, 200, 6, 2, 64, 1),
+    (1, 333, 8, 8, 64, 0),
 ]
 
 
-@pytest.mark.parametrize("B,L,n_q,n_kv,causal", SHAPES)
-def test_bwd_parity(B, L, n_q, n_kv, causal):
-    _run_case(B, L, n_q, n_kv, 128, causal, seed=200 + L + n_q)
+@pytest.mark.parametrize("B,L,n_q,n_kv,d,causal", SHAPES)
+def test_bwd_parity(B, L, n_q, n_kv, d, causal):
+    _run_case(B, L, n_q, n_kv, d, causal, seed=200 + L + n_q + d)
 
 
 @pytest.mark.parametrize("index", [2, 3])
@@ -132,8 +136,6 @@ def test_bwd_pipeline_and_errors():
         say(f"  pipeline {name}: max|d| / max|ref| = {rel:.3e}")
         assert rel <= 2e-2
     with pytest.raises(AttnPrefillError):
-        attn_prefill_backward(tq[..., :64].contiguous(), tk[..., :64].contiguous(),
-                              tv[..., :64].contiguous(), out[..., :64].contiguous(), lse,
-                              tdo[..., :64].contiguous())
+        attn_prefill_backward(tq, tk, tv, out, lse, tdo, scale=float("nan"))
     with pytest.raises(ValueError):
         attn_prefill_backward(tq, tk, tv, out, lse[:, :4].contiguous(), tdo)
