@@ -52,6 +52,9 @@ CHUNKS = [
     (1, 200, 1500, 0, 6, 3, 128, 0),
     (1, 3, 5000, 0, 2, 1, 64, 0),
     (1, 1000, 5000, 3000, 8, 2, 128, 1),
+    (3, 77, 500, 400, 6, 2, 64, 1),     # B = 3, d_h = 64, ragged chunk
+    (2, 130, 400, 50, 12, 2, 128, 0),   # non-causal: the offset is unused
+    (1, 256, 256, 0, 8, 4, 128, 0),
 ]
 
 

@@ -59,6 +59,10 @@ DECODES = [
     (1, 12345, 12345, 12, 2, 64),
     (5, 3000, 3001, 5, 5, 64),
     (1, 70000, 70000, 8, 1, 128),
+    (300, 100, 100, 4, 1, 64),      # many short sequences
+    (3, 4095, 5000, 24, 3, 128),    # g = 8, Lk one short of a tile multiple
+    (2, 33, 40, 12, 12, 128),       # MHA decode, Lk just past one tile
+    (1, 257, 257, 6, 2, 64),
 ]
 
 

@@ -77,6 +77,9 @@ SHAPES = [
     (1, 65, 1000, 33, 4, 2, 1),
     (1, 31, 7, 0, 4, 2, 0),
     (1, 4097, 4097, 0, 4, 4, 1),
+    (2, 300, 1000, 700, 12, 2, 1),      # g = 6 (two heads per workgroup), B = 2
+    (1, 129, 2000, 0, 8, 2, 0),         # non-causal chunk
+    (1, 2048, 8192, 6144, 16, 2, 1),    # a long chunk at an offset
 ]
 
 
