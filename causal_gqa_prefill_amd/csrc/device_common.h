@@ -76,9 +76,12 @@ __device__ __forceinline__ void dma_tile(const void* base, const int* src, int l
                                          int row_bytes, int j0, int L, int tile_rows,
                                          unsigned char* dst_shared) {
   LDS_AS unsigned char* dst = (LDS_AS unsigned char*)dst_shared;
+  // the record count is uniform; computed with vector min/max it would sit
+  // in a VGPR and make the compiler wrap every load in a waterfall loop, so
+  // it is moved to an SGPR explicitly
+  const int nbytes = __builtin_amdgcn_readfirstlane(min(max(L - j0, 0), tile_rows) * row_bytes);
   const __amdgpu_buffer_rsrc_t rsrc =
-      make_rsrc((const unsigned char*)base + (size_t)j0 * row_bytes,
-                (unsigned)min(max(L - j0, 0), tile_rows) * row_bytes);
+      make_rsrc((const unsigned char*)base + (size_t)j0 * row_bytes, (unsigned)nbytes);
 #pragma unroll
   for (int s = 0; s < loads; ++s)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + s * 1024), 16, src[s], 0,
