@@ -134,8 +134,10 @@ constexpr int kKvWaves = 4;                    // 32 keys per wave
 constexpr int kKvKeys = 32 * kKvWaves;         // keys per work item
 constexpr int kQT = 32;                        // query rows per tile
 
+// (two workgroups per CU: at least two waves per SIMD, so at most 256 VGPRs)
 template <int D>
-__global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2))) void
+bwd_dkdv_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
@@ -225,12 +227,9 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
              smem + DOOFF + buf * QT_BYTES + wave * QT_LOADS * 1024);
     if (wave == 0) {
       const int lim = max(min(L - q0, 64), 0) * 4;
-      const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + rowbase + q0, (unsigned)lim);
-      const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + rowbase + q0, (unsigned)lim);
-      LDS_AS unsigned char* st = sl + STOFF + buf * 512;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (LDS_AS void*)(st), 4, lane * 4, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (LDS_AS void*)(st + 256), 4, lane * 4, 0, 0,
-                                               0);
+      const unsigned st = lds_addr(smem + STOFF + buf * 512);
+      lds_load_b32(buffer_words(lse + rowbase + q0, lim), lane * 4, st);
+      lds_load_b32(buffer_words(delta + rowbase + q0, lim), lane * 4, st + 256);
     }
   };
 

@@ -58,12 +58,51 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
-// Raw buffer resource over `bytes` bytes from `base`: loads at offsets past
-// the end return zeros (the hardware range check), so the last, partial
-// K/V tile needs no clamping.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
+// Global -> LDS loads ("buffer_load ... lds": each lane's bytes at its
+// voffset land at the wave's LDS destination in M0 plus the lane's slot).
+//
+// They are issued from inline assembly.  The compiler does not track them,
+// so it adds no wait of its own for them; in particular it cannot treat
+// every later LDS transpose read as a possible reader of the bytes in
+// flight and wait for all outstanding loads before it, which would cut the
+// prefetch distance of a load ring to nothing.  Every caller instead waits
+// with an explicit s_waitcnt vmcnt for exactly the loads the next tile
+// needs, then crosses a barrier (or, for wave-private LDS, only waits),
+// before reading that tile, and waits for all of them before the wave ends.
+
+// Buffer resource words over `bytes` bytes from `base` (both wave-uniform;
+// the count is read into an SGPR so the whole resource stays scalar), raw
+// 32-bit format, stride 0: loads at offsets past the end return zeros (the
+// hardware range check).
+__device__ __forceinline__ u32x4 buffer_words(const void* base, int bytes) {
+  const unsigned long long addr = reinterpret_cast<unsigned long long>(base);
+  u32x4 w;
+  w[0] = (unsigned)addr;
+  w[1] = (unsigned)(addr >> 32) & 0xffffu;
+  w[2] = (unsigned)__builtin_amdgcn_readfirstlane(bytes);
+  w[3] = 0x00020000u;
+  return w;
+}
+
+// 16 bytes per lane at voffset, to LDS byte lds + 16 * lane
+__device__ __forceinline__ void lds_load_b128(const u32x4& rsrc, int voffset, unsigned lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds)
+               : "memory");
+}
+
+// 4 bytes per lane at voffset, to LDS byte lds + 4 * lane
+__device__ __forceinline__ void lds_load_b32(const u32x4& rsrc, int voffset, unsigned lds) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds)
+               : "memory");
+}
+
+// LDS byte address of a __shared__ pointer
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)reinterpret_cast<uintptr_t>((LDS_AS const unsigned char*)p);
 }
 
 // One wave's share of a K or V tile load, global -> LDS: `loads` loads of
@@ -75,17 +114,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 __device__ __forceinline__ void dma_tile(const void* base, const int* src, int loads,
                                          int row_bytes, int j0, int L, int tile_rows,
                                          unsigned char* dst_shared) {
-  LDS_AS unsigned char* dst = (LDS_AS unsigned char*)dst_shared;
-  // the record count is uniform; computed with vector min/max it would sit
-  // in a VGPR and make the compiler wrap every load in a waterfall loop, so
-  // it is moved to an SGPR explicitly
-  const int nbytes = __builtin_amdgcn_readfirstlane(min(max(L - j0, 0), tile_rows) * row_bytes);
-  const __amdgpu_buffer_rsrc_t rsrc =
-      make_rsrc((const unsigned char*)base + (size_t)j0 * row_bytes, (unsigned)nbytes);
+  const u32x4 rsrc = buffer_words((const unsigned char*)base + (size_t)j0 * row_bytes,
+                                  min(max(L - j0, 0), tile_rows) * row_bytes);
+  const unsigned dst = lds_addr(dst_shared);
 #pragma unroll
-  for (int s = 0; s < loads; ++s)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + s * 1024), 16, src[s], 0,
-                                             0, 0);
+  for (int s = 0; s < loads; ++s) lds_load_b128(rsrc, src[s], dst + s * 1024);
 }
 
 // Host: do [a, a + an) and [b, b + bn) overlap?
