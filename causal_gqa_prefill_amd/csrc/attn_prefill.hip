@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ out,
     float* __restrict__ lse, int Lq, int Lk, int q_off, int n_q, int n_kv, int n_qblk,
-    int items_per_qblk, float scale, int causal) {
+    int items_per_qblk, int n_items, float scale, int causal) {
   constexpr int NW = kCols / (32 * NB);        // waves per workgroup
   constexpr int BR = kCols / HWG;              // query rows per workgroup
   constexpr int KSTEPS = D / 16;               // k-steps of Q K^T
@@ -120,7 +120,12 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
   constexpr int VRING = 0;                     // V ring at [0, 4 TILE)
   constexpr int KRING = RING * TILE;           // K ring at [4 TILE, 8 TILE)
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * RING * TILE];
+  // output staging: one 32-row output tile per (wave, block); half of them
+  // in the last ring slot, the other half in an area after the rings
+  constexpr int OT = 32 * ROWB;                // bytes of one block's output tile
+  constexpr int STAGE = 2 * RING * TILE;       // staging area offset
+  static_assert(4 * OT == 2 * TILE && NW * NB == 8, "half the output tiles fill one ring slot");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGE + 4 * OT];
   LDS_AS unsigned char* const smem_l = (LDS_AS unsigned char*)smem;
 
   const int tid = threadIdx.x;
@@ -129,55 +134,83 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
   const int hi = lane >> 5;     // which half of the wave
   const int col = lane & 31;    // query column inside a 32-column block
 
-  // ---- work item: heavy q-blocks first; neighbouring ids differ in head
-  const int item = blockIdx.x;
-  const int qb = n_qblk - 1 - item / items_per_qblk;
-  int rest = item % items_per_qblk;
+  // ---- work items: (b, kv-head, head group, q-block), numbered heavy
+  // q-blocks first with neighbouring numbers on different heads.  The grid
+  // is persistent (at most one workgroup per CU) and round r covers items
+  // r G .. r G + G - 1: workgroup w takes item r G + w when r is even and
+  // the round's items backwards when r is odd, a zigzag over the
+  // heavy-first list that evens out the causal work of the workgroups.
+  // When G is a multiple of 8 the backward rounds are taken in blocks of 8
+  // (w = 8 a + x takes r G + 8 (G / 8 - 1 - a) + x), so a workgroup only
+  // sees items congruent to w mod 8: workgroups are dealt to the eight XCDs
+  // in turn, so each XCD keeps working on the same (batch, kv-head) streams
+  // when their count is a multiple of 8, and its L2 keeps serving their K/V.
   const int g = n_q / n_kv;
   const int ngroups = g / HWG;
-  const int hg = rest % ngroups;
-  rest /= ngroups;
-  const int kvh = rest % n_kv;
-  const int b = rest / n_kv;
-
+  const size_t Lq64 = (size_t)Lq;
+  auto item_at = [&] __device__ (int r) __attribute__((always_inline)) {
+    const int G = gridDim.x;
+    const int w = blockIdx.x;
+    if (!(r & 1)) return r * G + w;
+    if ((G & 7) == 0) return r * G + (G - 8 - (w & ~7)) + (w & 7);
+    return r * G + G - 1 - w;
+  };
+  struct Geo {
+    int qb, hg, kvh, b, n_tiles;  // n_tiles: K/V tiles the workgroup streams
+    const unsigned short* kb;     // K and V rows of the item's kv-head
+    const unsigned short* vb;
+  };
+  auto geo = [&] __device__ (int item) __attribute__((always_inline)) {
+    Geo e;
+    e.qb = n_qblk - 1 - item / items_per_qblk;
+    int rest = item % items_per_qblk;
+    e.hg = rest % ngroups;
+    rest /= ngroups;
+    e.kvh = rest % n_kv;
+    e.b = rest / n_kv;
+    // query row i sits at key position q_off + i; K and V hold Lk rows
+    const int wg_end = min(e.qb * BR + BR, Lq);
+    e.n_tiles = causal ? (wg_end + q_off + kBC - 1) / kBC : (Lk + kBC - 1) / kBC;
+    e.kb = k + ((size_t)e.b * n_kv + e.kvh) * (size_t)Lk * D;
+    e.vb = v + ((size_t)e.b * n_kv + e.kvh) * (size_t)Lk * D;
+    return e;
+  };
   // the wave's NB 32-column blocks: columns 32 (wave + NW ib) of the
   // workgroup, column c being head c / BR, row c % BR of the q-block
-  int hb[NB], q0b[NB];
-#pragma unroll
-  for (int ib = 0; ib < NB; ++ib) {
-    const int c0 = 32 * (wave + NW * ib);
-    hb[ib] = kvh * g + hg * HWG + c0 / BR;
-    q0b[ib] = qb * BR + c0 % BR;
-  }
-
-  // query row i sits at key position q_off + i; K and V hold Lk rows
-  const size_t Lq64 = (size_t)Lq;
-  const unsigned short* kbase = k + ((size_t)b * n_kv + kvh) * (size_t)Lk * D;
-  const unsigned short* vbase = v + ((size_t)b * n_kv + kvh) * (size_t)Lk * D;
-
-  // ---- tiles the workgroup streams, and tiles this wave computes
-  const int wg_end = min(qb * BR + BR, Lq);
-  const int n_tiles = causal ? (wg_end + q_off + kBC - 1) / kBC : (Lk + kBC - 1) / kBC;
-  int last_row = -1;
-#pragma unroll
-  for (int ib = 0; ib < NB; ++ib)
-    if (q0b[ib] < Lq) last_row = max(last_row, min(q0b[ib] + 31, Lq - 1));
-  const int wave_tiles =
-      last_row < 0 ? 0 : (causal ? (last_row + q_off) / kBC + 1 : n_tiles);
+  auto blk_head = [&] __device__ (const Geo& e, int ib) __attribute__((always_inline)) {
+    return e.kvh * g + e.hg * HWG + 32 * (wave + NW * ib) / BR;
+  };
+  auto blk_q0 = [&] __device__ (const Geo& e, int ib) __attribute__((always_inline)) {
+    return e.qb * BR + 32 * (wave + NW * ib) % BR;
+  };
 
   // ---- Q fragments (B operand of S^T = K Q^T): Q[row][16 kk + 8 hi + 0..7]
   bf16x8 qf[NB][KSTEPS];
+  auto load_q = [&] __device__ (const Geo& e) __attribute__((always_inline)) {
 #pragma unroll
-  for (int ib = 0; ib < NB; ++ib) {
-    const int qi = q0b[ib] + col;
-    const unsigned short* qrow = q + (((size_t)b * n_q + hb[ib]) * Lq64 + (size_t)qi) * D;
+    for (int ib = 0; ib < NB; ++ib) {
+      const int qi = blk_q0(e, ib) + col;
+      const unsigned short* qrow =
+          q + (((size_t)e.b * n_q + blk_head(e, ib)) * Lq64 + (size_t)qi) * D;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (qi < Lq) raw = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hi * 8);
-      qf[ib][kk] = __builtin_bit_cast(bf16x8, raw);
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (qi < Lq) raw = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hi * 8);
+        qf[ib][kk] = __builtin_bit_cast(bf16x8, raw);
+      }
     }
-  }
+  };
+
+  // per-item state the pipeline reads: the wave's block heads and first
+  // rows, the tiles the workgroup streams and the tiles this wave computes,
+  // the K/V rows of this item and of the next one
+  int hb[NB], q0b[NB];
+  int n_tiles = 0, wave_tiles = 0;
+  const unsigned short* kbase = k;
+  const unsigned short* vbase = v;
+  const unsigned short* nkbase = k;
+  const unsigned short* nvbase = v;
+  bool has_next = false;
 
   // ---- tile loads, global -> LDS.  Load s of this wave fills LDS bytes
   // [1 KB (wave * LOADS + s), +1 KB) of a tile; lane i fills 16 bytes at 16 i
@@ -222,18 +255,7 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
   // ---- running state per block: reference max m (log2 domain), lane
   // partial row sum l, accumulator O^T
   f32x16 acc[NB][TBLK];
-#pragma unroll
-  for (int ib = 0; ib < NB; ++ib)
-#pragma unroll
-    for (int tb = 0; tb < TBLK; ++tb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[ib][tb][r] = 0.0f;
   float m_run[NB], l_run[NB];
-#pragma unroll
-  for (int ib = 0; ib < NB; ++ib) {
-    m_run[ib] = -INFINITY;
-    l_run[ib] = 0.0f;
-  }
   const float c2 = scale * kLog2e;
   const bool fast_scale = c2 > 0.0f;
 
@@ -370,9 +392,21 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
   Half hA, hB;
   constexpr int KA = NB == 2 ? 3 : 2;  // k-steps of h+1 issued ahead of the branches
 
+  // Tile t of an item sits in ring slot t % 4; the ring runs on across
+  // items.  During tile t the workgroup requests stream position t + 3 into
+  // the slot tile t - 1 has freed: tile t + 3 of this item, or, past its last
+  // tile, tile j of the next item when the slot is j < 3 (so most of the
+  // next item's first tiles arrive while this one finishes).  Every tile
+  // step issues the same number of loads (otherwise a tile of this item past
+  // its end: rows that are never used, or zeros), which keeps the vmcnt
+  // counts exact and the step free of branches.
   auto issue_tile_loads = [&] __device__ (int TS, int t) __attribute__((always_inline)) {
-    load_tile(vbase, v_src, t + 3, VRING + ((TS + 3) & (RING - 1)) * TILE);
-    load_tile(kbase, k_src, t + 3, KRING + ((TS + 3) & (RING - 1)) * TILE);
+    const int p = t + 3;
+    const int slot = (TS + 3) & (RING - 1);
+    const bool own = p < n_tiles || !has_next || slot == RING - 1;
+    const int tile = own ? p : slot;
+    load_tile(own ? vbase : nvbase, v_src, tile, VRING + slot * TILE);
+    load_tile(own ? kbase : nkbase, k_src, tile, KRING + slot * TILE);
   };
 
   auto region = [&] __device__ (int t, int ts, int jb, Half& cur, Half& nxt)
@@ -382,6 +416,9 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     const int jb1 = jb ^ 1;
     const int slot2 = (ts + 1) & (RING - 1);
     const int jb2 = jb;
+    // keep the scheduler from pulling this region's row max up next to the
+    // previous region's last MFMAs (whose results it would then stall on)
+    __builtin_amdgcn_sched_barrier(0);
     qk_mfma(nxt.s, cur.kf, 0, KA);
     if (jb == 0) issue_tile_loads(ts, t);
     float cc[NB], mn[NB];
@@ -399,26 +436,10 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     }
   };
 
-  // ---- prologue: K0..K2 and V0..V2 into LDS; raw scores of half 0, K
-  // fragments of half 1 and V^T fragments of half 0 in registers
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    load_tile(kbase, k_src, i, KRING + i * TILE);
-    load_tile(vbase, v_src, i, VRING + i * TILE);
-  }
-  wait_vmcnt<0>();
-  tile_barrier();
-  if (wave_tiles > 0) {
-    load_kfrags(hB.kf, 0, 0);
-    qk_mfma(hA.s, hB.kf, 0, KSTEPS);
-    load_kfrags(hA.kf, 0, 1);
-    load_vfrags(hA.vf, 0, 0);
-  }
-
-  // one tile t (ring slot TS = t % 4, a constant once inlined): the loads of
-  // V(t+3) and K(t+3) (zeros past the end) fly during this tile and the next
-  // two; at its end the loads issued during the previous tile must have
-  // landed
+  // one tile t in ring slot TS (a constant once inlined): the loads of
+  // stream position t + 3 fly during this tile and the next two; at its end
+  // the loads issued during the previous tile (the tile the next step reads
+  // ahead) must have landed
   auto tile_step = [&] __device__ (int TS, int t) __attribute__((always_inline)) {
     if (t < wave_tiles) {
       region(t, TS, 0, hA, hB);
@@ -429,56 +450,138 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     wait_vmcnt<2 * LOADS>();
     tile_barrier();
   };
-  for (int t = 0; t < n_tiles; t += RING) {
-    tile_step(0, t);
-    if (t + 1 < n_tiles) tile_step(1, t + 1);
-    if (t + 2 < n_tiles) tile_step(2, t + 2);
-    if (t + 3 < n_tiles) tile_step(3, t + 3);
+
+  int r = 0;
+  int item = item_at(0);           // the grid never exceeds the item count
+  Geo cur = geo(item);
+  load_q(cur);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    load_tile(cur.kb, k_src, j, KRING + j * TILE);
+    load_tile(cur.vb, v_src, j, VRING + j * TILE);
+  }
+  for (;;) {
+    // ---- item setup
+    const int nxt_item = item_at(r + 1);
+    has_next = nxt_item < n_items;
+    const Geo nx = geo(has_next ? nxt_item : item);
+    kbase = cur.kb;
+    vbase = cur.vb;
+    nkbase = nx.kb;
+    nvbase = nx.vb;
+    n_tiles = cur.n_tiles;
+    int last_row = -1;
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib) {
+      hb[ib] = blk_head(cur, ib);
+      q0b[ib] = blk_q0(cur, ib);
+      if (q0b[ib] < Lq) last_row = max(last_row, min(q0b[ib] + 31, Lq - 1));
+    }
+    wave_tiles = last_row < 0 ? 0 : (causal ? (last_row + q_off) / kBC + 1 : n_tiles);
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib) {
+#pragma unroll
+      for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[ib][tb][e] = 0.0f;
+      m_run[ib] = -INFINITY;
+      l_run[ib] = 0.0f;
+    }
+
+    // ---- prologue: the item's tiles 0..2 and its Q have landed (and the
+    // previous item's stores are done); then the raw scores of half 0, the K
+    // fragments of half 1 and the V^T fragments of half 0 in registers
+    wait_vmcnt<0>();
+    tile_barrier();
+    if (wave_tiles > 0) {
+      load_kfrags(hB.kf, 0, 0);
+      qk_mfma(hA.s, hB.kf, 0, KSTEPS);
+      load_kfrags(hA.kf, 0, 1);
+      load_vfrags(hA.vf, 0, 0);
+    }
+
+    // ---- the item's tiles
+    for (int t = 0; t < n_tiles; t += RING) {
+      tile_step(0, t);
+      if (t + 1 < n_tiles) tile_step(1, t + 1);
+      if (t + 2 < n_tiles) tile_step(2, t + 2);
+      if (t + 3 < n_tiles) tile_step(3, t + 3);
+    }
+
+    // every load of the tile steps has landed, so nothing writes ring slot 3
+    // (which the output staging uses) any more; those loads were issued a
+    // tile or more ago
+    wait_vmcnt<0>();
+    if (has_next) {
+      // the next item's tiles 0..2 that the last tile steps could not
+      // request (the one whose slot held this item's last tile, and those
+      // of a short item), now that every slot is free; then its Q, all
+      // landing while this item's output is written
+      int req = 0;   // slots the tile steps filled with the next item's tiles
+      for (int t = max(0, n_tiles - 3); t < n_tiles; ++t) req |= 1 << ((t + 3) & (RING - 1));
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (!((req >> j) & 1)) {
+          load_tile(nkbase, k_src, j, KRING + j * TILE);
+          load_tile(nvbase, v_src, j, VRING + j * TILE);
+        }
+      load_q(nx);
+    }
+
+    // ---- epilogue: O = acc / l in bf16, LSE = ln 2 * (m + log2 l).  Each
+    // block's 32 x d_h output tile goes through LDS (ring slot 3, or the
+    // staging area) so that the global stores are whole rows: 1 KB
+    // per store instruction instead of 8-byte pieces of 32 different rows.
+    // (The lane id is re-derived here, opaque to the compiler, so that the
+    // staging addresses are computed in place instead of being kept, or
+    // spilled, across the tile loop.)
+    int elane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(elane));
+    const int ecol = elane & 31;
+    const int ehi = elane >> 5;
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib) {
+      const float l_tot = pair_sum(l_run[ib]);
+      const float inv = 1.0f / l_tot;
+      const int q0 = q0b[ib];
+      if (hi == 0 && q0 + col < Lq && wave_tiles > 0)
+        lse[((size_t)cur.b * n_q + hb[ib]) * Lq64 + (size_t)(q0 + col)] =
+            (m_run[ib] + __log2f(l_tot)) * kLn2;
+      const int idx = wave * NB + ib;
+      LDS_AS unsigned char* ot =
+          smem_l + (idx < 2 ? VRING + 3 * TILE + idx * OT
+                            : idx < 4 ? KRING + 3 * TILE + (idx - 2) * OT : STAGE + (idx - 4) * OT);
+      // lane (col, hi) holds row col, columns 32 tb + 8 grp + 4 hi + 0..3
+#pragma unroll
+      for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          bf16x4 o4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[ib][tb][grp * 4 + e] * inv);
+          const int chunk = tb * 4 + grp;                  // 16-byte chunk of the row
+          *reinterpret_cast<LDS_AS u32x2*>(ot + ecol * ROWB + ((chunk ^ k_swz<D>(ecol)) << 4) +
+                                           ehi * 8) = __builtin_bit_cast(u32x2, o4);
+        }
+      // read back whole rows: store st covers rows 1024 st / ROWB onwards
+      unsigned short* obase = out + (((size_t)cur.b * n_q + hb[ib]) * Lq64 + (size_t)q0) * D;
+#pragma unroll
+      for (int st = 0; st < OT / 1024; ++st) {
+        const int byte = st * 1024 + elane * 16;
+        const int row = byte / ROWB;
+        const int chunk = (byte % ROWB) >> 4;
+        const u32x4 v4 =
+            *reinterpret_cast<const LDS_AS u32x4*>(ot + row * ROWB + ((chunk ^ k_swz<D>(row)) << 4));
+        if (q0 + row < Lq && wave_tiles > 0)
+          *reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8) = v4;
+      }
+    }
+    if (!has_next) break;
+    cur = nx;
+    item = nxt_item;
+    ++r;
   }
   wait_vmcnt<0>();   // no tile load may still be writing LDS when the wave ends
-
-  // ---- epilogue: O = acc / l in bf16, LSE = ln 2 * (m + log2 l).  Each
-  // block's 32 x d_h output tile goes through LDS (free once every wave is
-  // past the loop and every tile load has landed), so that the global stores
-  // are whole rows: 1 KB per store instruction instead of 8-byte pieces of
-  // 32 different rows.
-  tile_barrier();
-  constexpr int OT = 32 * ROWB;                  // bytes of one block's output tile
-  static_assert(NW * NB * OT <= 2 * RING * TILE, "output staging must fit the rings");
-#pragma unroll
-  for (int ib = 0; ib < NB; ++ib) {
-    const float l_tot = pair_sum(l_run[ib]);
-    const float inv = 1.0f / l_tot;
-    LDS_AS unsigned char* ot = smem_l + (wave * NB + ib) * OT;
-    // lane (col, hi) holds row col, columns 32 tb + 8 grp + 4 hi + 0..3
-#pragma unroll
-    for (int tb = 0; tb < TBLK; ++tb)
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        bf16x4 o4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[ib][tb][grp * 4 + e] * inv);
-        const int chunk = tb * 4 + grp;                  // 16-byte chunk of the row
-        *reinterpret_cast<LDS_AS u32x2*>(ot + col * ROWB + ((chunk ^ k_swz<D>(col)) << 4) +
-                                         hi * 8) = __builtin_bit_cast(u32x2, o4);
-      }
-    const int q0 = q0b[ib];
-    if (hi == 0 && q0 + col < Lq && wave_tiles > 0)
-      lse[((size_t)b * n_q + hb[ib]) * Lq64 + (size_t)(q0 + col)] =
-          (m_run[ib] + __log2f(l_tot)) * kLn2;
-    // read back whole rows: store s covers rows 4 s .. 4 s + 3 (d_h = 128)
-    unsigned short* obase = out + (((size_t)b * n_q + hb[ib]) * Lq64 + (size_t)q0) * D;
-#pragma unroll
-    for (int st = 0; st < OT / 1024; ++st) {
-      const int byte = st * 1024 + lane * 16;
-      const int row = byte / ROWB;
-      const int chunk = (byte % ROWB) >> 4;
-      const u32x4 v4 =
-          *reinterpret_cast<const LDS_AS u32x4*>(ot + row * ROWB + ((chunk ^ k_swz<D>(row)) << 4));
-      if (q0 + row < Lq && wave_tiles > 0)
-        *reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8) = v4;
-    }
-  }
 }
 
 // Heads per workgroup: the largest of 8, 4, 2, 1 that divides g.
@@ -501,14 +604,23 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, c
   constexpr int BR = kCols / HWG;
   const int n_qblk = (sh.Lq + BR - 1) / BR;
   const long long items_per_qblk = (long long)sh.B * sh.n_kv * ((sh.n_q / sh.n_kv) / HWG);
-  const long long grid = items_per_qblk * n_qblk;
-  if (items_per_qblk > INT_MAX || grid > INT_MAX) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  const long long n_items = items_per_qblk * n_qblk;
+  // (round r of the persistent schedule computes r G + w, which must not wrap)
+  if (items_per_qblk > INT_MAX || n_items > INT_MAX / 2) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  // persistent grid: one workgroup per CU (a workgroup's LDS rings fill most
+  // of a CU's LDS), never more than there are items
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n_cu < 1)
+    return ATTN_PREFILL_ERR_LAUNCH;
+  const long long grid = n_items < n_cu ? n_items : n_cu;
   hipLaunchKernelGGL((attn_fwd_kernel<D, HWG, NB>), dim3((unsigned)grid), dim3(kCols / NB * 2), 0,
                      stream,
                      static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
                      static_cast<const unsigned short*>(v), static_cast<unsigned short*>(out), lse,
-                     sh.Lq, sh.Lk, sh.q_off, sh.n_q, sh.n_kv, n_qblk, (int)items_per_qblk, scale,
-                     causal);
+                     sh.Lq, sh.Lk, sh.q_off, sh.n_q, sh.n_kv, n_qblk, (int)items_per_qblk,
+                     (int)n_items, scale, causal);
   return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
 }
 
