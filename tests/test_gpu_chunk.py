@@ -55,6 +55,8 @@ CHUNKS = [
     (3, 77, 500, 400, 6, 2, 64, 1),     # B = 3, d_h = 64, ragged chunk
     (2, 130, 400, 50, 12, 2, 128, 0),   # non-causal: the offset is unused
     (1, 256, 256, 0, 8, 4, 128, 0),
+    (200, 100, 333, 200, 8, 2, 128, 1),  # 800 items: several chunk items per workgroup
+    (300, 40, 90, 50, 2, 2, 64, 1),      # 600 items of 2 tiles each (MHA, d_h = 64)
 ]
 
 

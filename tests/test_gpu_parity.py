@@ -61,6 +61,30 @@ def test_config_parity(cfg):
 
 
 # ---------------------------------------------------------------------------
+# the persistent schedule: far more work items than CUs, so every
+# workgroup walks several items back to back and the K/V ring runs across
+# item boundaries (items of 1 to 11 tiles, next-item tiles requested by the
+# last tile steps or after them, short items whose successor's first tiles
+# all come after the loop); every row against the oracle
+# ---------------------------------------------------------------------------
+MANY_ITEMS = [
+    # B, L, n_q, n_kv, d, causal: items = B * n_kv * (g / HWG) * ceil(L / BR)
+    (160, 260, 8, 1, 128, 1),    # 1440 items of 1..5 tiles (32-row q-blocks)
+    (300, 64, 1, 1, 128, 1),     # 300 one-tile items (256-row q-blocks, MHA)
+    (64, 700, 2, 1, 64, 1),      # 384 items of 1..11 tiles, d_h = 64
+    (96, 300, 4, 2, 128, 0),     # 576 non-causal items of 5 tiles each
+    (40, 130, 12, 4, 128, 1),    # g = 3 (one head per item): 480 items of 3 tiles
+]
+
+
+@pytest.mark.parametrize("B,L,n_q,n_kv,d,causal", MANY_ITEMS)
+def test_many_items_per_workgroup(B, L, n_q, n_kv, d, causal):
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    _check_case(B, L, n_q, n_kv, d, causal, scale, seed=4000 + B + L,
+                name=f"many items B={B} L={L} n_q={n_q} n_kv={n_kv} d={d} causal={causal}")
+
+
+# ---------------------------------------------------------------------------
 # edge shapes: ragged L, every GQA ratio class, both head sizes, B > 1,
 # non-causal, scales other than 1/sqrt(d)
 # ---------------------------------------------------------------------------
