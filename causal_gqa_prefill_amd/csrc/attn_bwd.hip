@@ -130,54 +130,69 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const unsigned short* __
 }
 
 // ---- dK, dV
-constexpr int kKvWaves = 4;                    // 32 keys per wave
-constexpr int kKvKeys = 32 * kKvWaves;         // keys per work item
-constexpr int kQT = 32;                        // query rows per tile
+constexpr int kKvGroupWaves = 4;                // waves of a group: 32 keys each
+constexpr int kKvKeys = 32 * kKvGroupWaves;     // keys per work item
+constexpr int kQT = 32;                         // query rows per tile
 
-// (two workgroups per CU: at least two waves per SIMD, so at most 256 VGPRs)
-template <int D>
-__global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2))) void
+// NG groups of four waves share the item's key block (the same K rows in
+// each group's registers, one copy of its V rows in LDS) and take every
+// NG-th query tile.  NG = 1: 65 KB of LDS and at most 256 registers, two
+// workgroups per CU.  NG = 2: one workgroup per CU that a key block most
+// queries see keeps busy on its own (for grids of a few rounds, where such
+// a block would otherwise run alone at one wave per SIMD); at the end the
+// second group's fp32 partial sums of dK^T and dV^T are added into the
+// first group's through LDS and the first group writes the result.
+template <int D, int NG>
+__global__ __launch_bounds__(64 * kKvGroupWaves * NG) __attribute__((amdgpu_waves_per_eu(2))) void
 bwd_dkdv_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
     unsigned short* __restrict__ dk, unsigned short* __restrict__ dv, int L, int n_q, int n_kv,
-    int n_kblk, int mirror, float scale, int causal) {
+    int n_kblk, float scale, int causal) {
   constexpr int ROWB = 2 * D;
   constexpr int KSTEPS = D / 16;
   constexpr int TBLK = D / 32;
   constexpr int V_BYTES = kKvKeys * ROWB;         // 32 KB: the item's V rows
   constexpr int QT_BYTES = kQT * ROWB;            // 8 KB: one Q (or dO) tile
   constexpr int VOFF = 0;
-  constexpr int QOFF = V_BYTES;                   // 2 buffers of Q tiles
-  constexpr int DOOFF = QOFF + 2 * QT_BYTES;      // 2 buffers of dO tiles
-  constexpr int STOFF = DOOFF + 2 * QT_BYTES;     // 2 buffers x (64 lse + 64 delta) floats
-  constexpr int SMEM = STOFF + 2 * 2 * 64 * 4;    // 65 KB: two workgroups per CU
-  constexpr int V_LOADS = V_BYTES / (kKvWaves * 1024);     // 8 per wave
-  constexpr int QT_LOADS = QT_BYTES / (kKvWaves * 1024);   // 2 per wave
-  static_assert(kKvWaves * 32 * ROWB <= SMEM, "output staging must fit");
+  // per group: 2 buffers of Q tiles, 2 of dO tiles, 2 x (32 lse + 32 delta
+  // floats, padded to 256 bytes each)
+  constexpr int G_QOFF = 0;
+  constexpr int G_DOOFF = 2 * QT_BYTES;
+  constexpr int G_STOFF = 4 * QT_BYTES;
+  constexpr int G_BYTES = G_STOFF + 2 * 512;
+  constexpr int GOFF = V_BYTES;                   // group areas after the V rows
+  constexpr int SMEM = GOFF + NG * G_BYTES;       // 65 or 98 KB (d_h = 128)
+  constexpr int NWV = kKvGroupWaves * NG;         // waves per workgroup
+  constexpr int V_LOADS = V_BYTES / (NWV * 1024);              // 8 or 4 per wave
+  constexpr int QT_LOADS = QT_BYTES / (kKvGroupWaves * 1024);  // 2 per wave
+  // the reduction (a group's dK^T or dV^T partials: 64 floats per lane per
+  // wave) and the output staging (32 rows per wave) fit side by side
+  constexpr int RED_BYTES = kKvGroupWaves * TBLK * 16 * 64 * 4;
+  static_assert((NG == 2 ? RED_BYTES : 0) + kKvGroupWaves * 32 * ROWB <= SMEM,
+                "reduction and staging must fit");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
   LDS_AS unsigned char* const sl = (LDS_AS unsigned char*)smem;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / kKvGroupWaves;           // which group
+  const int gw = wave % kKvGroupWaves;            // wave inside the group
   const int lane = tid & 63;
   const int hi = lane >> 5;
   const int col = lane & 31;
 
   // work item: key blocks in order (block 0, the one most queries see,
-  // first).  When the whole grid runs at once (mirror), the second half of
-  // the blocks comes in reverse, so that the two workgroups sharing a CU
-  // (items i and i + half) take blocks k and n - 1 - k: equal causal work.
+  // first), so the hardware's in-order dispatch places the heaviest first
   const int item = blockIdx.x;
-  const int pos = item / (gridDim.x / n_kblk);
-  const int kb = (mirror && pos >= (n_kblk + 1) / 2) ? n_kblk - 1 - (pos - (n_kblk + 1) / 2) : pos;
+  const int kb = item / (gridDim.x / n_kblk);
   const int rest = item % (gridDim.x / n_kblk);
   const int kvh = rest % n_kv;
   const int b = rest / n_kv;
   const int g = n_q / n_kv;
   const int k0 = kb * kKvKeys;
-  const int kw0 = k0 + 32 * wave;                 // this wave's first key
+  const int kw0 = k0 + 32 * gw;                   // this wave's first key
 
   // this wave's K rows as the B operand of S = Q K^T, straight from memory
   // into registers (zero past L): key kw0 + col, elements 16 kk + 8 hi .. +8
@@ -192,7 +207,7 @@ bwd_dkdv_kernel(
     }
   }
   // the item's V rows into LDS (rows past L read as zero), the B operand of
-  // dP = dO V^T
+  // dP = dO V^T; every wave of the workgroup loads a share
   {
     int src[V_LOADS];
 #pragma unroll
@@ -202,32 +217,35 @@ bwd_dkdv_kernel(
   }
   int qsrc[QT_LOADS];
 #pragma unroll
-  for (int s = 0; s < QT_LOADS; ++s) qsrc[s] = tile_src<D, true>(wave * QT_LOADS, s, lane);
+  for (int s = 0; s < QT_LOADS; ++s) qsrc[s] = tile_src<D, true>(gw * QT_LOADS, s, lane);
+  LDS_AS unsigned char* const gl = sl + GOFF + grp * G_BYTES;   // this group's area
 
   // query tiles: every head of the group, rows from the first tile that can
-  // see a key of the block (causal) or from 0
+  // see a key of the block (causal) or from 0; group grp takes tiles
+  // n = NG i + grp
   const int qt_first = causal ? k0 / kQT : 0;
   const int qt_per_head = (L + kQT - 1) / kQT - qt_first;
   const int n_qt = g * qt_per_head;
+  const int n_iter = (n_qt + NG - 1) / NG;
   auto tile_head = [&] __device__ (int n) __attribute__((always_inline)) {
     return kvh * g + n / qt_per_head;
   };
   auto tile_q0 = [&] __device__ (int n) __attribute__((always_inline)) {
     return (qt_first + n % qt_per_head) * kQT;
   };
-  // loads of tile n into buffer n % 2: Q and dO rows (zero past L), and the
-  // rows' LSE and delta (wave 0, 4 bytes per lane; zero past L)
-  auto load_qtile = [&] __device__ (int n) __attribute__((always_inline)) {
+  // loads of this group's tile n into its buffer `buf`: Q and dO rows (zero
+  // past L), and the rows' LSE and delta (the group's first wave, 4 bytes
+  // per lane; zero past L)
+  auto load_qtile = [&] __device__ (int n, int buf) __attribute__((always_inline)) {
     const int q0 = tile_q0(n);
     const size_t rowbase = ((size_t)b * n_q + tile_head(n)) * (size_t)L;
-    const int buf = n & 1;
     dma_tile(q + rowbase * D, qsrc, QT_LOADS, ROWB, q0, L, kQT,
-             smem + QOFF + buf * QT_BYTES + wave * QT_LOADS * 1024);
+             smem + GOFF + grp * G_BYTES + G_QOFF + buf * QT_BYTES + gw * QT_LOADS * 1024);
     dma_tile(dout + rowbase * D, qsrc, QT_LOADS, ROWB, q0, L, kQT,
-             smem + DOOFF + buf * QT_BYTES + wave * QT_LOADS * 1024);
-    if (wave == 0) {
+             smem + GOFF + grp * G_BYTES + G_DOOFF + buf * QT_BYTES + gw * QT_LOADS * 1024);
+    if (gw == 0) {
       const int lim = max(min(L - q0, 64), 0) * 4;
-      const unsigned st = lds_addr(smem + STOFF + buf * 512);
+      const unsigned st = lds_addr(smem + GOFF + grp * G_BYTES + G_STOFF + buf * 512);
       lds_load_b32(buffer_words(lse + rowbase + q0, lim), lane * 4, st);
       lds_load_b32(buffer_words(delta + rowbase + q0, lim), lane * 4, st + 256);
     }
@@ -240,20 +258,24 @@ bwd_dkdv_kernel(
     for (int r = 0; r < 16; ++r) dkT[tb][r] = dvT[tb][r] = 0.0f;
   const float c2 = scale * kLog2e;
 
-  if (n_qt > 0) load_qtile(0);
-  for (int n = 0; n < n_qt; ++n) {
-    // tile n has landed everywhere, and every wave is done with tile n - 1
+  if (grp < n_qt) load_qtile(grp, 0);
+  for (int i = 0; i < n_iter; ++i) {
+    // this wave's loads of tile NG i + grp (and the V rows) have landed;
+    // after the barrier every wave's have, and every wave is done with the
+    // buffer the next loads overwrite
     wait_vmcnt<0>();
     tile_barrier();
-    if (n + 1 < n_qt) load_qtile(n + 1);
+    const int n = NG * i + grp;
+    if (n + NG < n_qt) load_qtile(n + NG, (i + 1) & 1);
+    if (n >= n_qt) continue;
     const int q0 = tile_q0(n);
-    const int buf = n & 1;
+    const int buf = i & 1;
     // skip when every query of the tile is before every key of the wave
     if (causal && q0 + kQT - 1 < kw0) continue;
-    LDS_AS const unsigned char* qt = sl + QOFF + buf * QT_BYTES;
-    LDS_AS const unsigned char* dot = sl + DOOFF + buf * QT_BYTES;
-    LDS_AS const unsigned char* vt = sl + VOFF + 32 * wave * ROWB;
-    LDS_AS const float* st = (LDS_AS const float*)(sl + STOFF + buf * 512);
+    LDS_AS const unsigned char* qt = gl + G_QOFF + buf * QT_BYTES;
+    LDS_AS const unsigned char* dot = gl + G_DOOFF + buf * QT_BYTES;
+    LDS_AS const unsigned char* vt = sl + VOFF + 32 * gw * ROWB;
+    LDS_AS const float* st = (LDS_AS const float*)(gl + G_STOFF + buf * 512);
 
     // S = Q K^T and dP = dO V^T: rows = queries (A from the Q / dO tile),
     // columns = this wave's keys (B from its K / V registers)
@@ -303,25 +325,63 @@ bwd_dkdv_kernel(
   }
   wait_vmcnt<0>();
 
-  // ---- epilogue: dK = scale dK^T^T, then dV = dV^T^T, in bf16, each staged
-  // through LDS (8 KB per wave) as whole rows
-  tile_barrier();
-  LDS_AS unsigned char* ot = sl + wave * 32 * ROWB;
+  // ---- the second group's partial sums into the first group's registers,
+  // dK^T then dV^T, through LDS at [0, RED_BYTES): wave gw of each group
+  // holds the same keys in the same lane layout, 16 bytes per lane and
+  // store, laid out (wave, register quad, lane)
+  LDS_AS unsigned char* const red = sl + gw * (TBLK * 16 * 64 * 4) + lane * 16;
+#pragma unroll
+  for (int which = 0; which < (NG == 2 ? 2 : 0); ++which) {
+    tile_barrier();   // the area is free (loop done / previous part read)
+    if (grp == 1) {
+#pragma unroll
+      for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x16& a = which == 0 ? dkT[tb] : dvT[tb];
+          const f32x4 v4 = {a[4 * qd], a[4 * qd + 1], a[4 * qd + 2], a[4 * qd + 3]};
+          *reinterpret_cast<LDS_AS f32x4*>(red + (tb * 4 + qd) * 1024) = v4;
+        }
+    }
+    tile_barrier();
+    if (grp == 0) {
+#pragma unroll
+      for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x4 v4 = *reinterpret_cast<const LDS_AS f32x4*>(red + (tb * 4 + qd) * 1024);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (which == 0)
+              dkT[tb][4 * qd + e] += v4[e];
+            else
+              dvT[tb][4 * qd + e] += v4[e];
+          }
+        }
+    }
+  }
+  if (grp != 0) return;
+
+  // ---- epilogue (first group): dK = scale dK^T^T, then dV = dV^T^T, in
+  // bf16, each staged through LDS (8 KB per wave) as whole rows; a wave
+  // reads back only the rows it wrote, in order, so no barrier is needed
+  // after the one that ends the loop (or the reduction)
+  if (NG == 1) tile_barrier();
+  LDS_AS unsigned char* ot = sl + (NG == 2 ? RED_BYTES : 0) + gw * 32 * ROWB;
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
 #pragma unroll
     for (int tb = 0; tb < TBLK; ++tb)
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
+      for (int grp4 = 0; grp4 < 4; ++grp4) {
         bf16x4 o4;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          o4[e] = (__bf16)(which == 0 ? dkT[tb][grp * 4 + e] * scale : dvT[tb][grp * 4 + e]);
-        const int chunk = tb * 4 + grp;
+          o4[e] = (__bf16)(which == 0 ? dkT[tb][grp4 * 4 + e] * scale : dvT[tb][grp4 * 4 + e]);
+        const int chunk = tb * 4 + grp4;
         *reinterpret_cast<LDS_AS u32x2*>(ot + col * ROWB + ((chunk ^ swz_row<D>(col)) << 4) +
                                          hi * 8) = __builtin_bit_cast(u32x2, o4);
       }
-    // a wave reads back only the rows it wrote, in order: no barrier needed
     unsigned short* gbase = (which == 0 ? dk : dv) + (((size_t)b * n_kv + kvh) * L + kw0) * D;
 #pragma unroll
     for (int st = 0; st < 32 * ROWB / 1024; ++st) {
@@ -532,15 +592,32 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* out, con
                      static_cast<const unsigned short*>(out),
                      static_cast<const unsigned short*>(dout), delta, rows);
   if (hipGetLastError() != hipSuccess) return ATTN_PREFILL_ERR_LAUNCH;
-  // one round of the whole grid (two workgroups on each of the 256 CUs):
-  // pair heavy and light key blocks on each CU
-  const int mirror = causal && kv_grid <= 2 * 256;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)kv_grid), dim3(64 * kKvWaves), 0, stream,
-                     static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
-                     static_cast<const unsigned short*>(v),
-                     static_cast<const unsigned short*>(dout), lse, delta,
-                     static_cast<unsigned short*>(dk), static_cast<unsigned short*>(dv), L, n_q,
-                     n_kv, (int)n_kblk, mirror, scale, causal);
+  // A causal key block's work grows with the queries that see it (block 0:
+  // all of them).  When the grid is only a few rounds of two workgroups per
+  // CU, the heaviest blocks would end up running alone on a CU at one wave
+  // per SIMD, well past the average load; then two groups share each block
+  // in a workgroup that fills the CU (the same holds for a non-causal grid
+  // that does not fill the CUs).
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n_cu < 1)
+    return ATTN_PREFILL_ERR_LAUNCH;
+  const bool split = causal ? kv_grid <= 3LL * n_cu : kv_grid <= n_cu;
+  if (split)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2>), dim3((unsigned)kv_grid), dim3(64 * kKvGroupWaves * 2),
+                       0, stream, static_cast<const unsigned short*>(q),
+                       static_cast<const unsigned short*>(k), static_cast<const unsigned short*>(v),
+                       static_cast<const unsigned short*>(dout), lse, delta,
+                       static_cast<unsigned short*>(dk), static_cast<unsigned short*>(dv), L, n_q,
+                       n_kv, (int)n_kblk, scale, causal);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 1>), dim3((unsigned)kv_grid), dim3(64 * kKvGroupWaves),
+                       0, stream, static_cast<const unsigned short*>(q),
+                       static_cast<const unsigned short*>(k), static_cast<const unsigned short*>(v),
+                       static_cast<const unsigned short*>(dout), lse, delta,
+                       static_cast<unsigned short*>(dk), static_cast<unsigned short*>(dv), L, n_q,
+                       n_kv, (int)n_kblk, scale, causal);
   if (hipGetLastError() != hipSuccess) return ATTN_PREFILL_ERR_LAUNCH;
   switch (bwd_pick_hwg(n_q / n_kv)) {
     case 8: return launch_dq<D, 8>(q, k, v, dout, lse, delta, dq, B, L, n_q, n_kv, scale, causal, stream);

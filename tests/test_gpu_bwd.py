@@ -89,6 +89,11 @@ SHAPES = [
     (1, 128, 4, 4, 64, 1),      # the tiny causal MHA workload's shape
     (2, 200, 6, 2, 64, 1),
     (1, 333, 8, 8, 64, 0),
+    # grids of more key blocks than three rounds of the CUs: the dK/dV kernel
+    # with one group of waves per workgroup (smaller grids use two)
+    (200, 256, 2, 2, 64, 1),    # 800 key blocks
+    (150, 384, 4, 2, 128, 1),   # 900 key blocks
+    (150, 256, 2, 2, 128, 0),   # 600 non-causal key blocks
 ]
 
 
