@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
     const unsigned char* __restrict__ q, const unsigned char* __restrict__ k,
     const unsigned char* __restrict__ v, unsigned short* __restrict__ out,
     float* __restrict__ lse, int Lq, int Lk, int q_off, int n_q, int n_kv, int n_qblk,
-    int items_per_qblk, float c2, float v_mul, int causal) {
+    int items_per_qblk, int n_items, float c2, float v_mul, int causal) {
   constexpr int D = kF8D;
   constexpr int BR = kF8Cols / HWG;            // query rows per workgroup
   constexpr int KSTEPS = D / 64;               // 64-deep k-steps of Q K^T
@@ -91,7 +91,14 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
   constexpr int VRING = 0;
   constexpr int KRING = RING * TILE;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * RING * TILE];
+  // output staging: one wave's 32 bf16 output rows (8 KB); waves 0..3 use
+  // ring slot 3 (idle once an item's last tile is done), waves 4..7 an area
+  // after the rings
+  constexpr int OROWB = 2 * D;                 // bytes per bf16 output row
+  constexpr int OT = 32 * OROWB;               // bytes of one wave's output tile
+  constexpr int STAGE = 2 * RING * TILE;
+  static_assert(4 * OT == 2 * TILE && kF8Waves == 8, "half the output tiles fill one ring slot");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGE + 4 * OT];
   LDS_AS unsigned char* const smem_l = (LDS_AS unsigned char*)smem;
 
   const int tid = threadIdx.x;
@@ -100,37 +107,49 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
   const int hi = lane >> 5;
   const int col = lane & 31;
 
-  // ---- work item, as the bf16 kernel: heavy q-blocks first
-  const int item = blockIdx.x;
-  const int qb = n_qblk - 1 - item / items_per_qblk;
-  int rest = item % items_per_qblk;
+  // ---- work items as the bf16 kernel: (b, kv-head, head group, q-block),
+  // heavy q-blocks first; a persistent grid (at most one workgroup per CU)
+  // takes round r's items r G + w (r even) or backwards in blocks of 8 (r
+  // odd), so the workgroups' causal work evens out and each XCD keeps its
+  // (batch, kv-head) streams
   const int g = n_q / n_kv;
   const int ngroups = g / HWG;
-  const int hg = rest % ngroups;
-  rest /= ngroups;
-  const int kvh = rest % n_kv;
-  const int b = rest / n_kv;
   const int c0 = 32 * wave;
-  const int hh = kvh * g + hg * HWG + c0 / BR;   // this wave's query head
-  const int q0 = qb * BR + c0 % BR;              // this wave's first query row
-
   const size_t Lq64 = (size_t)Lq;
-  const unsigned char* kbase = k + ((size_t)b * n_kv + kvh) * (size_t)Lk * D;
-  const unsigned char* vbase = v + ((size_t)b * n_kv + kvh) * (size_t)Lk * D;
-
-  const int wg_end = min(qb * BR + BR, Lq);
-  const int n_tiles = causal ? (wg_end + q_off + kF8Tile - 1) / kF8Tile
-                             : (Lk + kF8Tile - 1) / kF8Tile;
-  const int last_row = q0 < Lq ? min(q0 + 31, Lq - 1) : -1;
-  const int n_units_all = 2 * n_tiles;
-  const int wave_units =
-      last_row < 0 ? 0 : (causal ? (last_row + q_off) / kF8Unit + 1 : n_units_all);
+  auto item_at = [&] __device__ (int r) __attribute__((always_inline)) {
+    const int G = gridDim.x;
+    const int w = blockIdx.x;
+    if (!(r & 1)) return r * G + w;
+    if ((G & 7) == 0) return r * G + (G - 8 - (w & ~7)) + (w & 7);
+    return r * G + G - 1 - w;
+  };
+  struct Geo {
+    int b, hh, q0, n_tiles;       // batch, this wave's head and first row, tiles streamed
+    const unsigned char* kb;
+    const unsigned char* vb;
+  };
+  auto geo = [&] __device__ (int item) __attribute__((always_inline)) {
+    Geo e;
+    const int qb = n_qblk - 1 - item / items_per_qblk;
+    int rest = item % items_per_qblk;
+    const int hg = rest % ngroups;
+    rest /= ngroups;
+    const int kvh = rest % n_kv;
+    e.b = rest / n_kv;
+    e.hh = kvh * g + hg * HWG + c0 / BR;
+    e.q0 = qb * BR + c0 % BR;
+    const int wg_end = min(qb * BR + BR, Lq);
+    e.n_tiles = causal ? (wg_end + q_off + kF8Tile - 1) / kF8Tile : (Lk + kF8Tile - 1) / kF8Tile;
+    e.kb = k + ((size_t)e.b * n_kv + kvh) * (size_t)Lk * D;
+    e.vb = v + ((size_t)e.b * n_kv + kvh) * (size_t)Lk * D;
+    return e;
+  };
 
   // ---- Q fragments (B operand of S^T = K Q^T): bytes 64 kk + 32 hi .. +32 of row q0 + col
   i32x8 qf[KSTEPS];
-  {
-    const int qi = q0 + col;
-    const unsigned char* qrow = q + (((size_t)b * n_q + hh) * Lq64 + (size_t)qi) * D;
+  auto load_q = [&] __device__ (const Geo& e) __attribute__((always_inline)) {
+    const int qi = e.q0 + col;
+    const unsigned char* qrow = q + (((size_t)e.b * n_q + e.hh) * Lq64 + (size_t)qi) * D;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       u32x4 lo = {0u, 0u, 0u, 0u}, up = {0u, 0u, 0u, 0u};
@@ -141,7 +160,15 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
       qf[kk] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                        (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
     }
-  }
+  };
+
+  // per-item state the pipeline reads
+  int q0 = 0, n_tiles = 0, wave_units = 0;
+  const unsigned char* kbase = k;
+  const unsigned char* vbase = v;
+  const unsigned char* nkbase = k;
+  const unsigned char* nvbase = v;
+  bool has_next = false;
 
   // ---- tile loads: load s of this wave fills LDS bytes [1 KB (wave * LOADS
   // + s), +1 KB) of a tile with the chunks the rows' swizzles put there
@@ -181,10 +208,6 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
   }
 
   f32x16 acc[TBLK];
-#pragma unroll
-  for (int tb = 0; tb < TBLK; ++tb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[tb][r] = 0.0f;
   float m_run = -INFINITY;   // reference max, log2 domain
   float l_run = 0.0f;        // this lane's part of the row sum
   const bool fast_scale = c2 > 0.0f;
@@ -299,12 +322,25 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
   i32x8 kf[2][KSTEPS];
   i32x8 vf[TBLK];
 
+  // Tile t of an item sits in ring slot t % 4; the ring runs on across
+  // items.  During tile t the workgroup requests stream position t + 3 into
+  // the slot tile t - 1 has freed: tile t + 3 of this item, or, past its last
+  // tile, tile j of the next item when the slot is j < 3.  Every tile step
+  // issues the same number of loads (otherwise a tile of this item past its
+  // end: rows never used, or zeros), which keeps the vmcnt counts exact.
   auto issue_tile_loads = [&] __device__ (int TS, int t) __attribute__((always_inline)) {
-    load_tile(vbase, v_src, t + 3, VRING + ((TS + 3) & (RING - 1)) * TILE);
-    load_tile(kbase, k_src, t + 3, KRING + ((TS + 3) & (RING - 1)) * TILE);
+    const int p = t + 3;
+    const int slot = (TS + 3) & (RING - 1);
+    const bool own = p < n_tiles || !has_next || slot == RING - 1;
+    const int tile = own ? p : slot;
+    load_tile(own ? vbase : nvbase, v_src, tile, VRING + slot * TILE);
+    load_tile(own ? kbase : nkbase, k_src, tile, KRING + slot * TILE);
   };
   auto region = [&] __device__ (int t, int ts, int uu, f32x16 (&cur)[2], f32x16 (&nxt)[2])
       __attribute__((always_inline)) {
+    // keep the scheduler from pulling this region's softmax up next to the
+    // previous region's last MFMAs
+    __builtin_amdgcn_sched_barrier(0);
     qk(nxt, kf);
     if (uu == 0) issue_tile_loads(ts, t);
     load_vfrags(vf, ts, uu);
@@ -315,23 +351,9 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
     pv(vf, pk);
   };
 
-  // ---- prologue: tiles 0..2 into LDS; scores of unit 0, K fragments of unit 1
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    load_tile(kbase, k_src, i, KRING + i * TILE);
-    load_tile(vbase, v_src, i, VRING + i * TILE);
-  }
-  wait_vmcnt<0>();
-  tile_barrier();
-  if (wave_units > 0) {
-    load_kfrags(kf, 0, 0);
-    qk(SA, kf);
-    load_kfrags(kf, 0, 1);
-  }
-
   auto tile_step = [&] __device__ (int TS, int t) __attribute__((always_inline)) {
     if (2 * t < wave_units) {
-      region(t, TS, 0, SA, SB);   // issues the loads of tile t + 3
+      region(t, TS, 0, SA, SB);   // issues the loads of stream position t + 3
       if (2 * t + 1 < wave_units) region(t, TS, 1, SB, SA);
     } else {
       issue_tile_loads(TS, t);
@@ -339,47 +361,112 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
     wait_vmcnt<2 * LOADS>();
     tile_barrier();
   };
-  for (int t = 0; t < n_tiles; t += RING) {
-    tile_step(0, t);
-    if (t + 1 < n_tiles) tile_step(1, t + 1);
-    if (t + 2 < n_tiles) tile_step(2, t + 2);
-    if (t + 3 < n_tiles) tile_step(3, t + 3);
-  }
-  wait_vmcnt<0>();
 
-  // ---- epilogue: O = v_mul acc / l in bf16 through LDS (whole-row stores),
-  // LSE = ln 2 (m + log2 l)
-  tile_barrier();
-  constexpr int OT = 32 * 2 * D;   // bytes of one wave's bf16 output tile
-  static_assert(kF8Waves * OT <= 2 * RING * TILE, "output staging must fit the rings");
-  const float l_tot = pair_sum(l_run);
-  const float inv = v_mul / l_tot;
-  LDS_AS unsigned char* ot = smem_l + wave * OT;
-  constexpr int OROWB = 2 * D;
+  int r = 0;
+  int item = item_at(0);           // the grid never exceeds the item count
+  Geo cur = geo(item);
+  load_q(cur);
 #pragma unroll
-  for (int tb = 0; tb < TBLK; ++tb)
-#pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      bf16x4 o4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[tb][grp * 4 + e] * inv);
-      const int chunk = tb * 4 + grp;
-      *reinterpret_cast<LDS_AS u32x2*>(ot + col * OROWB + ((chunk ^ (col & 15)) << 4) + hi * 8) =
-          __builtin_bit_cast(u32x2, o4);
-    }
-  if (hi == 0 && q0 + col < Lq && wave_units > 0)
-    lse[((size_t)b * n_q + hh) * Lq64 + (size_t)(q0 + col)] = (m_run + __log2f(l_tot)) * kLn2;
-  unsigned short* obase = out + (((size_t)b * n_q + hh) * Lq64 + (size_t)q0) * D;
-#pragma unroll
-  for (int st = 0; st < OT / 1024; ++st) {
-    const int byte = st * 1024 + lane * 16;
-    const int row = byte / OROWB;
-    const int chunk = (byte % OROWB) >> 4;
-    const u32x4 v4 =
-        *reinterpret_cast<const LDS_AS u32x4*>(ot + row * OROWB + ((chunk ^ (row & 15)) << 4));
-    if (q0 + row < Lq && wave_units > 0)
-      *reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8) = v4;
+  for (int i = 0; i < 3; ++i) {
+    load_tile(cur.kb, k_src, i, KRING + i * TILE);
+    load_tile(cur.vb, v_src, i, VRING + i * TILE);
   }
+  for (;;) {
+    // ---- item setup
+    const int nxt_item = item_at(r + 1);
+    has_next = nxt_item < n_items;
+    const Geo nx = geo(has_next ? nxt_item : item);
+    kbase = cur.kb;
+    vbase = cur.vb;
+    nkbase = nx.kb;
+    nvbase = nx.vb;
+    n_tiles = cur.n_tiles;
+    q0 = cur.q0;
+    const int last_row = q0 < Lq ? min(q0 + 31, Lq - 1) : -1;
+    wave_units = last_row < 0 ? 0 : (causal ? (last_row + q_off) / kF8Unit + 1 : 2 * n_tiles);
+#pragma unroll
+    for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[tb][e] = 0.0f;
+    m_run = -INFINITY;
+    l_run = 0.0f;
+
+    // ---- prologue: the item's tiles 0..2 and its Q have landed (and the
+    // previous item's stores are done); scores of unit 0, K fragments of unit 1
+    wait_vmcnt<0>();
+    tile_barrier();
+    if (wave_units > 0) {
+      load_kfrags(kf, 0, 0);
+      qk(SA, kf);
+      load_kfrags(kf, 0, 1);
+    }
+    for (int t = 0; t < n_tiles; t += RING) {
+      tile_step(0, t);
+      if (t + 1 < n_tiles) tile_step(1, t + 1);
+      if (t + 2 < n_tiles) tile_step(2, t + 2);
+      if (t + 3 < n_tiles) tile_step(3, t + 3);
+    }
+    // every load of the tile steps has landed (issued a tile or more ago),
+    // so nothing writes ring slot 3, which the output staging uses
+    wait_vmcnt<0>();
+    if (has_next) {
+      // the next item's tiles 0..2 the last tile steps could not request,
+      // then its Q, landing while this item's output is written
+      int req = 0;
+      for (int t = max(0, n_tiles - 3); t < n_tiles; ++t) req |= 1 << ((t + 3) & (RING - 1));
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (!((req >> j) & 1)) {
+          load_tile(nkbase, k_src, j, KRING + j * TILE);
+          load_tile(nvbase, v_src, j, VRING + j * TILE);
+        }
+      load_q(nx);
+    }
+
+    // ---- epilogue: O = v_mul acc / l in bf16 through LDS (whole-row
+    // stores), LSE = ln 2 (m + log2 l).  (The lane id is re-derived, opaque
+    // to the compiler, so the staging addresses are computed here instead of
+    // being kept across the tile loop.)
+    int elane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(elane));
+    const int ecol = elane & 31;
+    const int ehi = elane >> 5;
+    const float l_tot = pair_sum(l_run);
+    const float inv = v_mul / l_tot;
+    LDS_AS unsigned char* ot =
+        smem_l + (wave < 2 ? VRING + 3 * TILE + wave * OT
+                           : wave < 4 ? KRING + 3 * TILE + (wave - 2) * OT : STAGE + (wave - 4) * OT);
+#pragma unroll
+    for (int tb = 0; tb < TBLK; ++tb)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[tb][grp * 4 + e] * inv);
+        const int chunk = tb * 4 + grp;
+        *reinterpret_cast<LDS_AS u32x2*>(ot + ecol * OROWB + ((chunk ^ (ecol & 15)) << 4) +
+                                         ehi * 8) = __builtin_bit_cast(u32x2, o4);
+      }
+    if (hi == 0 && q0 + col < Lq && wave_units > 0)
+      lse[((size_t)cur.b * n_q + cur.hh) * Lq64 + (size_t)(q0 + col)] =
+          (m_run + __log2f(l_tot)) * kLn2;
+    unsigned short* obase = out + (((size_t)cur.b * n_q + cur.hh) * Lq64 + (size_t)q0) * D;
+#pragma unroll
+    for (int st = 0; st < OT / 1024; ++st) {
+      const int byte = st * 1024 + elane * 16;
+      const int row = byte / OROWB;
+      const int chunk = (byte % OROWB) >> 4;
+      const u32x4 v4 =
+          *reinterpret_cast<const LDS_AS u32x4*>(ot + row * OROWB + ((chunk ^ (row & 15)) << 4));
+      if (q0 + row < Lq && wave_units > 0)
+        *reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8) = v4;
+    }
+    if (!has_next) break;
+    cur = nx;
+    item = nxt_item;
+    ++r;
+  }
+  wait_vmcnt<0>();   // no tile load may still be writing LDS when the wave ends
 }
 
 int f8_pick_hwg(int g) {
@@ -396,13 +483,21 @@ int f8_launch(const void* q, const void* k, const void* v, void* out, float* lse
   constexpr int BR = kF8Cols / HWG;
   const int n_qblk = (Lq + BR - 1) / BR;
   const long long items_per_qblk = (long long)B * n_kv * ((n_q / n_kv) / HWG);
-  const long long grid = items_per_qblk * n_qblk;
-  if (items_per_qblk > INT_MAX || grid > INT_MAX) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  const long long n_items = items_per_qblk * n_qblk;
+  // (round r of the persistent schedule computes r G + w, which must not wrap)
+  if (items_per_qblk > INT_MAX || n_items > INT_MAX / 2) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  // persistent grid: one workgroup per CU, never more than there are items
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n_cu < 1)
+    return ATTN_PREFILL_ERR_LAUNCH;
+  const long long grid = n_items < n_cu ? n_items : n_cu;
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<HWG>), dim3((unsigned)grid), dim3(64 * kF8Waves), 0,
                      stream, static_cast<const unsigned char*>(q),
                      static_cast<const unsigned char*>(k), static_cast<const unsigned char*>(v),
                      static_cast<unsigned short*>(out), lse, Lq, Lk, q_off, n_q, n_kv, n_qblk,
-                     (int)items_per_qblk, c2, v_mul, causal);
+                     (int)items_per_qblk, (int)n_items, c2, v_mul, causal);
   return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
 }
 
