@@ -18,7 +18,9 @@
 //    rows) with 8 waves, one 32-column block each, as the bf16 kernel.
 //  * K and V tiles of 128 keys x 128 bytes (16 KB, the bytes of a bf16 tile)
 //    stream into 4-tile LDS rings by buffer loads with the LDS destination
-//    bit, requested three tiles ahead, one barrier per tile.
+//    bit, requested three tiles ahead, one barrier per tile.  As in the bf16
+//    kernel the grid is persistent (one workgroup per CU, a zigzag over the
+//    heavy-first items) and the ring runs on across items.
 //  * The unit of compute is 64 keys: S^T = K Q^T for two 32-key blocks (two
 //    64-deep k-steps each), the softmax of both, then O^T += V^T P^T as one
 //    64-deep contraction per 32 rows of O^T.  A lane holds 16 scores of each

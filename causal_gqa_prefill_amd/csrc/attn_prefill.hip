@@ -55,6 +55,11 @@
 //    and V, tiles requested three ahead, one barrier per tile.  The compute
 //    runs in 32-key halves: the scores of the next half are formed on the
 //    MFMA pipe while the softmax of the current half is on the VALU.
+//  * The grid is persistent, one workgroup per CU walking a zigzag over the
+//    heavy-first list of work items, and the ring runs on across items: the
+//    next item's first tiles are requested into the slots the current
+//    item's last tiles free, and its Q is loaded while the current output is
+//    written, so an item no longer starts by waiting on HBM.
 //  * LDS rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads
 //    do not collide on banks (see k_swz / v_swz).
 //  * exp is exp2 with scale*log2(e) folded into one FMA; l and acc are only
