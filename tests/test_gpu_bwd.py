@@ -94,6 +94,7 @@ SHAPES = [
     (200, 256, 2, 2, 64, 1),    # 800 key blocks
     (150, 384, 4, 2, 128, 1),   # 900 key blocks
     (150, 256, 2, 2, 128, 0),   # 600 non-causal key blocks
+    (100, 384, 4, 2, 64, 1),    # 600 causal key blocks: two groups per block, several rounds
 ]
 
 
