@@ -43,6 +43,10 @@
  * synchronises, and may be called from several host threads at once.  out and
  * lse must not overlap each other or any input.
  *
+ * Launch: the prefill kernels run a persistent grid of at most one
+ * workgroup per CU of the current device (each walks several work items);
+ * the result does not depend on the grid size.
+ *
  * Errors: every argument is checked on the host before anything is enqueued.
  * A nonzero return means nothing was enqueued, except ATTN_PREFILL_ERR_LAUNCH,
  * which reports the HIP launch error.  Faults inside the kernel surface at the
@@ -69,7 +73,9 @@ enum attn_prefill_status {
                                            lse not 4-byte aligned              */
     ATTN_PREFILL_ERR_SIZE_OVERFLOW = 8, /* a size or the grid overflows        */
     ATTN_PREFILL_ERR_ALIASING = 9,      /* out or lse overlaps another buffer  */
-    ATTN_PREFILL_ERR_LAUNCH = 10,       /* the HIP launch failed               */
+    ATTN_PREFILL_ERR_LAUNCH = 10,       /* the HIP launch failed, or the query
+                                           of the current device's CU count
+                                           that sizes the grid                 */
     ATTN_PREFILL_ERR_BAD_OFFSET = 11,   /* q_offset < 0, or (causal)
                                            q_offset + Lq > Lk, or (decode)
                                            kv_capacity < Lk                    */
