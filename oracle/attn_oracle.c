@@ -23,10 +23,11 @@
  *   emits that statistic as the natural-log log-sum-exp of the scaled scores,
  *   LSE = m + ln(sum_j exp(s_j - m)).
  *
- * Readings where the pages are silent (each is listed with its reason in the
- * design notes): query head h reads key/value head floor(h / g); the scale is
- * the caller's fp32 value, widened exactly; inputs are bf16 bit patterns,
- * widened exactly to fp64; everything after that is fp64.
+ * Readings where the pages are silent: query head h reads key/value head
+ * floor(h / g) (consecutive query heads form a group, the repeat-interleave
+ * reading of heads sharing K and V); the scale is the caller's fp32 value,
+ * widened exactly; inputs are bf16 bit patterns, widened exactly to fp64;
+ * everything after that is fp64.
  *
  * Chunked prefill ("flops / prefill-attention", section "Workarounds": a long
  * prompt split into pieces): a chunk of Lq queries against Lk keys, query
