@@ -27,10 +27,10 @@
 //    block; together they are the 32 bytes of its P^T operand, byte
 //    16 b + r holding key 32 b + 8 (r / 4) + 4 (lane / 32) + r % 4.  The
 //    matrix cores pair byte e of a lane half of one operand with byte e of
-//    the same lane half of the other (checked on the box), so any byte order
+//    the same lane half of the other (verified on an MI355X), so any byte order
 //    works as long as V^T uses the same one.
 //  * V^T in that key order comes from the row-major V tile through
-//    ds_read_b64_tr_b8 (checked on the box: in each group of 16 lanes, lane
+//    ds_read_b64_tr_b8 (verified on an MI355X: in each group of 16 lanes, lane
 //    2 e + q supplies 8 bytes, and lane i receives byte i % 8 of the piece of
 //    lane 2 e + i / 8 as its byte e).  Four reads give a lane its 32 keys.
 //  * P = 2^(c s - m) never exceeds 2^8 (the reference max moves when a tile
