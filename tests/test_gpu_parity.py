@@ -200,6 +200,58 @@ def test_non_default_stream():
     compare("side stream", o.reshape(-1, 128), l.reshape(-1), ref_o, ref_l)
 
 
+def test_concurrent_calls_on_two_streams_from_two_threads():
+    """The library keeps no state: two calls in flight at once (two host
+    threads, two streams, persistent grids competing for the same CUs) give
+    the same bits as the calls run one after the other."""
+    import threading
+    import torch
+    from causal_gqa_prefill_amd import attn_prefill_into
+    shapes = [(4, 1024, 16, 4, 128, 1, 51), (2, 1500, 8, 8, 64, 1, 52)]
+    runs = []
+    for (B, L, n_q, n_kv, d, causal, seed) in shapes:
+        qb, kb, vb = inputs.make_qkv(B, L, n_q, n_kv, d, seed)
+        q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+        runs.append((q, k, v, causal))
+    # one after the other
+    ref = []
+    for (q, k, v, causal) in runs:
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        attn_prefill_into(q, k, v, out, lse, causal=bool(causal))
+        torch.cuda.synchronize()
+        ref.append((out.clone(), lse.clone()))
+    # both in flight: each thread launches 5 calls on its own stream
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [(torch.full_like(q, float("nan")),
+             torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device))
+            for (q, k, v, causal) in runs]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        try:
+            q, k, v, causal = runs[i]
+            for _ in range(5):
+                attn_prefill_into(q, k, v, outs[i][0], outs[i][1], causal=bool(causal),
+                                  stream=streams[i])
+        except Exception as e:  # reported after the join
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        same_o = torch.equal(outs[i][0].view(torch.int16), ref[i][0].view(torch.int16))
+        same_l = torch.equal(outs[i][1].view(torch.int32), ref[i][1].view(torch.int32))
+        say(f"  concurrent call {i}: output bits equal {same_o}, lse bits equal {same_l}")
+        assert same_o and same_l
+
+
 def test_argument_errors_raise():
     import torch
     from causal_gqa_prefill_amd import AttnPrefillError, attn_prefill
