@@ -306,7 +306,10 @@ bwd_dkdv_kernel(
         const int r = 4 * a + c;
         const int qi = q0 + 8 * a + 4 * hi + c;
         const bool dead = (causal && key > qi) || key >= L;
-        const float p = dead ? 0.0f : __builtin_amdgcn_exp2f(fmaf(S[r], c2, -lv[c] * kLog2e));
+        // masked scores go in as -inf (2^-inf = 0): a select, where a
+        // conditional exponential would become a branch per element
+        const float x = fmaf(S[r], c2, -lv[c] * kLog2e);
+        const float p = __builtin_amdgcn_exp2f(dead ? -INFINITY : x);
         const float ds = p * (dP[r] - dv4[c]);
         pk[r >> 3][r & 7] = (__bf16)p;
         dsk[r >> 3][r & 7] = (__bf16)ds;
@@ -514,7 +517,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
       for (int r = 0; r < 16; ++r) {
         const int j = j0 + (r >> 2) * 8 + hi * 4 + (r & 3);
         const bool dead = (causal && j > qi) || j >= L;
-        const float p = dead ? 0.0f : __builtin_amdgcn_exp2f(fmaf(S[r], c2, -lse2));
+        const float x = fmaf(S[r], c2, -lse2);
+        const float p = __builtin_amdgcn_exp2f(dead ? -INFINITY : x);   // 2^-inf = 0
         dsk[r >> 3][r & 7] = (__bf16)(p * (dP[r] - dlt));
       }
       // dQ^T += K^T dS^T (contraction over the half's keys)
