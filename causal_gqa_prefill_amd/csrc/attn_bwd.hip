@@ -132,6 +132,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const unsigned short* __
 // ---- dK, dV
 constexpr int kKvGroupWaves = 4;                // waves of a group: 32 keys each
 constexpr int kKvKeys = 32 * kKvGroupWaves;     // keys per work item
+constexpr int kKvAhead = 1;     // S / dP operand reads issued this many k-steps ahead
+constexpr int kKvTrAhead = 3;   // dV / dK operand reads issued this many MFMAs ahead
 constexpr int kQT = 32;                         // query rows per tile
 
 // NG groups of four waves share the item's key block (the same K rows in
@@ -278,19 +280,39 @@ bwd_dkdv_kernel(
     LDS_AS const float* st = (LDS_AS const float*)(gl + G_STOFF + buf * 512);
 
     // S = Q K^T and dP = dO V^T: rows = queries (A from the Q / dO tile),
-    // columns = this wave's keys (B from its K / V registers)
+    // columns = this wave's keys (B from its K registers / the V rows).  The
+    // LDS fragments are read kKvAhead k-steps ahead of their MFMAs (the
+    // scheduling barriers keep that order).
     f32x16 S, dP;
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
+    bf16x8 qa[KSTEPS], oa[KSTEPS], va[KSTEPS];
+    auto load_qov = [&] __device__ (int kk) __attribute__((always_inline)) {
+      const int ch = 2 * kk + hi;
+      qa[kk] = frag16<D>(qt, col, ch, swz_tr<D>(col));
+      oa[kk] = frag16<D>(dot, col, ch, swz_tr<D>(col));
+      va[kk] = frag16<D>(vt, col, ch, swz_row<D>(col));
+    };
+#pragma unroll
+    for (int kk = 0; kk < kKvAhead; ++kk) load_qov(kk);
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-      const int ch = 2 * kk + hi;
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16<D>(qt, col, ch, swz_tr<D>(col)), kf[kk], S, 0,
-                                                 0, 0);
-      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16<D>(dot, col, ch, swz_tr<D>(col)),
-                                                  frag16<D>(vt, col, ch, swz_row<D>(col)), dP, 0, 0,
-                                                  0);
+      if (kk + kKvAhead < KSTEPS) load_qov(kk + kKvAhead);
+      __builtin_amdgcn_sched_barrier(0);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], S, 0, 0, 0);
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[kk], va[kk], dP, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the first transposed fragments of the dV / dK products, read while
+    // the VALU forms P and dS: MFMA i of that phase is (ks, tb, which) =
+    // (i / (2 TBLK), i / 2 % TBLK, i % 2), which = 0 for dV (dO^T), 1 for dK (Q^T)
+    bf16x8 tf[4 * TBLK];
+    auto load_tr = [&] __device__ (int i) __attribute__((always_inline)) {
+      tf[i] = frag_tr<D>(i % 2 == 0 ? dot : qt, (i / 2) % TBLK, i / (2 * TBLK), lane);
+    };
+#pragma unroll
+    for (int i = 0; i < kKvTrAhead; ++i) load_tr(i);
+    __builtin_amdgcn_sched_barrier(0);
     // P = 2^(c2 s - log2e lse), dS = P (dP - D); lane (key col) holds
     // queries 8 (r / 4) + 4 hi + r % 4
     bf16x8 pk[2], dsk[2];
@@ -315,16 +337,19 @@ bwd_dkdv_kernel(
         dsk[r >> 3][r & 7] = (__bf16)ds;
       }
     }
-    // dV^T += dO^T P, dK^T += Q^T dS (contraction over the tile's queries)
+    // dV^T += dO^T P, dK^T += Q^T dS (contraction over the tile's queries),
+    // each fragment read kKvTrAhead MFMAs ahead
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int tb = 0; tb < TBLK; ++tb) {
-        dvT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(dot, tb, ks, lane), pk[ks],
-                                                         dvT[tb], 0, 0, 0);
-        dkT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(qt, tb, ks, lane), dsk[ks],
-                                                         dkT[tb], 0, 0, 0);
-      }
+    for (int i = 0; i < 4 * TBLK; ++i) {
+      if (i + kKvTrAhead < 4 * TBLK) load_tr(i + kKvTrAhead);
+      __builtin_amdgcn_sched_barrier(0);
+      const int tb = (i / 2) % TBLK, ks = i / (2 * TBLK);
+      if (i % 2 == 0)
+        dvT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], pk[ks], dvT[tb], 0, 0, 0);
+      else
+        dkT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i], dsk[ks], dkT[tb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   wait_vmcnt<0>();
 
@@ -402,6 +427,7 @@ bwd_dkdv_kernel(
 constexpr int kDqCols = 256;   // query columns per workgroup (8 waves x 32)
 constexpr int kDqWaves = 8;
 constexpr int kDqKeys = 64;    // keys per K/V tile
+constexpr int kDqAhead = 3;    // LDS operand reads issued this many MFMA steps ahead
 
 template <int D, int HWG>
 __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
@@ -499,18 +525,34 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
       const int j0 = t * kDqKeys + 32 * jb;
       LDS_AS const unsigned char* kh = kt + 32 * jb * ROWB;
       LDS_AS const unsigned char* vh = vt + 32 * jb * ROWB;
-      // S^T = K Q^T and dP^T = V dO^T: rows = keys, columns = queries
+      // S^T = K Q^T and dP^T = V dO^T: rows = keys, columns = queries.  The
+      // K and V fragments are read kDqAhead k-steps ahead of their MFMAs
+      // (the scheduling barriers keep that order), so the LDS latency
+      // overlaps the MFMAs instead of preceding each one.
       f32x16 S, dP;
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
+      bf16x8 ka[KSTEPS], va[KSTEPS];
+      auto load_kv = [&] __device__ (int kk) __attribute__((always_inline)) {
+        ka[kk] = frag16<D>(kh, col, 2 * kk + hi, swz_tr<D>(col));
+        va[kk] = frag16<D>(vh, col, 2 * kk + hi, swz_row<D>(col));
+      };
+#pragma unroll
+      for (int kk = 0; kk < kDqAhead; ++kk) load_kv(kk);
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        const int ch = 2 * kk + hi;
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16<D>(kh, col, ch, swz_tr<D>(col)), qf[kk], S,
-                                                   0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16<D>(vh, col, ch, swz_row<D>(col)), of[kk],
-                                                    dP, 0, 0, 0);
+        if (kk + kDqAhead < KSTEPS) load_kv(kk + kDqAhead);
+        __builtin_amdgcn_sched_barrier(0);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk], of[kk], dP, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      // the first K^T fragments of the dQ product, read while the VALU
+      // forms dS
+      bf16x8 kt_f[2 * TBLK];
+#pragma unroll
+      for (int i = 0; i < kDqAhead; ++i) kt_f[i] = frag_tr<D>(kh, i % TBLK, i / TBLK, lane);
+      __builtin_amdgcn_sched_barrier(0);
       // dS^T = P^T (dP^T - D), lane (query col) holds keys 8 (r / 4) + 4 hi + r % 4
       bf16x8 dsk[2];
 #pragma unroll
@@ -521,13 +563,17 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
         const float p = __builtin_amdgcn_exp2f(dead ? -INFINITY : x);   // 2^-inf = 0
         dsk[r >> 3][r & 7] = (__bf16)(p * (dP[r] - dlt));
       }
-      // dQ^T += K^T dS^T (contraction over the half's keys)
+      // dQ^T += K^T dS^T (contraction over the half's keys), MFMA i = (ks,
+      // tb) = (i / TBLK, i % TBLK), its fragment read kDqAhead MFMAs ahead
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int tb = 0; tb < TBLK; ++tb)
-          dqT[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(kh, tb, ks, lane), dsk[ks],
-                                                           dqT[tb], 0, 0, 0);
+      for (int i = 0; i < 2 * TBLK; ++i) {
+        if (i + kDqAhead < 2 * TBLK)
+          kt_f[i + kDqAhead] = frag_tr<D>(kh, (i + kDqAhead) % TBLK, (i + kDqAhead) / TBLK, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        dqT[i % TBLK] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_f[i], dsk[i / TBLK],
+                                                               dqT[i % TBLK], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   wait_vmcnt<0>();
