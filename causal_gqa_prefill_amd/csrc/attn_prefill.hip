@@ -335,13 +335,15 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     const bool need_mask = (causal && j0 + 31 > q0 + q_off) || (j0 + 32 > Lk);
     float c = c2;
     if (need_mask || !fast_scale) {
+      // score r of this lane is key j0 + 4 hi + o_r, o_r = 8 (r / 4) + r % 4,
+      // visible to query qi (at key position qi + q_off) iff o_r <= lim.  A
+      // scale <= 0 is applied before masking, so that a masked score stays
+      // -inf; a positive one later, in the exponential.
+      const int lim = (causal ? min(qi + q_off, Lk - 1) : Lk - 1) - j0 - 4 * hi;
+      const float cm = fast_scale ? 1.0f : c2;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = j0 + (r >> 2) * 8 + hi * 4 + (r & 3);
-        const bool dead = (causal && j > qi + q_off) || j >= Lk;
-        s[r] = dead ? -INFINITY : s[r] * c2;
-      }
-      c = 1.0f;
+      for (int r = 0; r < 16; ++r) s[r] = (r >> 2) * 8 + (r & 3) > lim ? -INFINITY : s[r] * cm;
+      c = fast_scale ? c2 : 1.0f;
       mx = row_max(s);
     }
     const float m_cand = mx * c;
