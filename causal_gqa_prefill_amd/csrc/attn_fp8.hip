@@ -408,9 +408,13 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
       if (t + 2 < n_tiles) tile_step(2, t + 2);
       if (t + 3 < n_tiles) tile_step(3, t + 3);
     }
-    // every load of the tile steps has landed (issued a tile or more ago),
-    // so nothing writes ring slot 3, which the output staging uses
+    // No wave's tile load may still write ring slot 3, which the output
+    // staging uses.  Its last load was issued by tile step (n_tiles - 1) & ~3;
+    // a step ends (at its barrier) with only its own loads in flight, so
+    // unless that step is the last one they have all landed.  If it is, every
+    // wave must see every other wave's loads land: the barrier after the wait.
     wait_vmcnt<0>();
+    if (n_tiles <= 0 || ((n_tiles - 1) & (RING - 1)) == 0) tile_barrier();
     if (has_next) {
       // the next item's tiles 0..2 the last tile steps could not request,
       // then its Q, landing while this item's output is written

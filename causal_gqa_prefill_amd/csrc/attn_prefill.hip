@@ -515,10 +515,13 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
       if (t + 3 < n_tiles) tile_step(3, t + 3);
     }
 
-    // every load of the tile steps has landed, so nothing writes ring slot 3
-    // (which the output staging uses) any more; those loads were issued a
-    // tile or more ago
+    // No wave's tile load may still write ring slot 3, which the output
+    // staging uses.  Its last load was issued by tile step (n_tiles - 1) & ~3;
+    // a step ends (at its barrier) with only its own loads in flight, so
+    // unless that step is the last one they have all landed.  If it is, every
+    // wave must see every other wave's loads land: the barrier after the wait.
     wait_vmcnt<0>();
+    if (n_tiles <= 0 || ((n_tiles - 1) & (RING - 1)) == 0) tile_barrier();
     if (has_next) {
       // the next item's tiles 0..2 that the last tile steps could not
       // request (the one whose slot held this item's last tile, and those
