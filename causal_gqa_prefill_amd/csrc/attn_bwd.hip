@@ -41,18 +41,29 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// 16-byte chunk swizzles of rows of 2 D bytes: "row" for tiles read by
-// 16-byte row reads (16 lanes take 16 consecutive rows at one chunk), "tr"
-// for tiles read by the transpose read (32 lanes take 4 rows x 2 chunk
-// pairs); the same spreads over the banks as the forward kernel's K and V
-// swizzles (for D = 64 two rows share a 256-byte window).
+// 16-byte chunk swizzles of rows of 2 D bytes (the LDS has 64 banks of 4
+// bytes, so a 256-byte window spans them all; for D = 64 two rows share
+// one).  "row": for tiles read only by 16-byte row reads, where a pass of 16
+// lanes takes 16 consecutive rows at one chunk: the 16 rows must land on 16
+// different chunk positions.  "tr": for tiles read both that way and by the
+// transpose read, where a pass of 32 lanes takes an aligned group of 4 rows,
+// 64 bytes (a 4-aligned group of 4 chunks) of each: besides the row-read
+// condition the 4 rows must fall in 4 different 64-byte windows (D = 64:
+// the two rows of each parity in 2 different ones).  It also maps the
+// column block tb of row r + 8 (r % 16 < 8) to where block tb ^ 1 of row r
+// sits, so the transpose read's second row group is the first one's address
+// for tb ^ 1 plus 8 rows (no address of its own).  As 4 f + g (f: 64-byte
+// window, g: chunk in it), with r = 8 r3 + 4 r2 + 2 r1 + r0:
+//   D = 128: f = (2 r1 + r0) ^ r3, g = 2 r0 + r2;
+//   D = 64:  f = r1 ^ r3,          g = 2 r2 + r1.
 template <int D>
 __device__ __forceinline__ int swz_row(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
 template <int D>
 __device__ __forceinline__ int swz_tr(int row) {
-  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+  if (D == 128) return 4 * ((row & 3) ^ ((row >> 3) & 1)) + 2 * (row & 1) + ((row >> 2) & 1);
+  return 4 * (((row >> 1) ^ (row >> 3)) & 1) + 2 * ((row >> 2) & 1) + ((row >> 1) & 1);
 }
 
 // A 16-byte operand fragment of row `row` (relative to a tile at `base`),
@@ -76,12 +87,15 @@ __device__ __forceinline__ bf16x8 frag_tr(LDS_AS const unsigned char* base, int 
   const int tr_r = (lane >> 2) & 3;
   const int tr_q = lane & 3;
   const int tr_g = (lane >> 4) & 1;
-  const int t = 32 * tb + 16 * tr_g + 4 * tr_q;
   const int key = 16 * ks + 4 * hi + tr_r;
-  const LDS_AS unsigned char* p =
-      base + key * ROWB + (((t >> 3) ^ swz_tr<D>(key)) << 4) + ((t >> 2) & 1) * 8;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
-  const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 8 * ROWB));
+  // this lane's 8 bytes of row key in column block c
+  auto at = [&](int c) __attribute__((always_inline)) {
+    const int t = 32 * c + 16 * tr_g + 4 * tr_q;
+    return base + key * ROWB + (((t >> 3) ^ swz_tr<D>(key)) << 4) + ((t >> 2) & 1) * 8;
+  };
+  // rows key + 8: under the swizzle, block tb there is block tb ^ 1 of row key moved 8 rows
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)at(tb));
+  const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(at(tb ^ 1) + 8 * ROWB));
   return __builtin_bit_cast(
       bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                       __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]});
@@ -133,7 +147,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const unsigned short* __
 constexpr int kKvGroupWaves = 4;                // waves of a group: 32 keys each
 constexpr int kKvKeys = 32 * kKvGroupWaves;     // keys per work item
 constexpr int kKvAhead = 1;     // S / dP operand reads issued this many k-steps ahead
-constexpr int kKvTrAhead = 3;   // dV / dK operand reads issued this many MFMAs ahead
+constexpr int kKvTrAhead = 2;   // dV / dK operand reads issued this many MFMAs ahead
 constexpr int kQT = 32;                         // query rows per tile
 
 // NG groups of four waves share the item's key block (the same K rows in
@@ -427,7 +441,7 @@ bwd_dkdv_kernel(
 constexpr int kDqCols = 256;   // query columns per workgroup (8 waves x 32)
 constexpr int kDqWaves = 8;
 constexpr int kDqKeys = 64;    // keys per K/V tile
-constexpr int kDqAhead = 3;    // LDS operand reads issued this many MFMA steps ahead
+constexpr int kDqAhead = 2;    // LDS operand reads issued this many MFMA steps ahead
 
 template <int D, int HWG>
 __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
