@@ -72,7 +72,8 @@ MANY_ITEMS = [
     (160, 260, 8, 1, 128, 1),    # 1440 items of 1..5 tiles (32-row q-blocks)
     (300, 64, 1, 1, 128, 1),     # 300 one-tile items (256-row q-blocks, MHA)
     (64, 700, 2, 1, 64, 1),      # 384 items of 1..11 tiles, d_h = 64
-    (96, 300, 4, 2, 128, 0),     # 576 non-causal items of 5 tiles each
+    (96, 300, 4, 2, 128, 0),     # 576 non-causal items of 5 tiles each (last step loads the
+                                 # staging slot: the barrier before the output staging)
     (40, 130, 12, 4, 128, 1),    # g = 3 (one head per item): 480 items of 3 tiles
 ]
 
