@@ -63,8 +63,21 @@ CONFIGS = [
 ]
 
 
+# One GPU's share of the Llama-2-70B-shaped GQA-8 layer when the layer is
+# split by key/value head over eight GPUs: each GPU holds one key/value head
+# and its eight query heads, and no byte crosses between GPUs.  A whole GPU
+# then works on a single key/value stream.
+SHARE_CONFIG = AttnConfig(6, "one GPU's share (1 of 8 key/value heads) of the "
+                          "Llama-2-70B-shaped GQA-8 layer", 1, 32768, 8, 1, 128,
+                          sampled_rows=4096)
+
+
 def config(index: int) -> AttnConfig:
-    """Config by its 1-based index."""
+    """Config by its 1-based index (6: the one-GPU share above)."""
+    if index == SHARE_CONFIG.index:
+        return SHARE_CONFIG
+    if not 1 <= index <= len(CONFIGS):
+        raise ValueError(f"no workload {index}")
     return CONFIGS[index - 1]
 
 
