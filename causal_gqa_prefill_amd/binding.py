@@ -58,6 +58,11 @@ def library():
                                         ctypes.c_float, vp, ctypes.c_size_t, vp]
         lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
         lib.attn_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+        lib.attn_decode_fwd_noalloc.restype = ci
+        lib.attn_decode_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, ci, ci, ctypes.c_longlong,
+                                                ci, ci, ci, ctypes.c_float, vp]
+        lib.attn_decode_scratch_bytes.restype = ctypes.c_size_t
+        lib.attn_decode_scratch_bytes.argtypes = []
         lib.attn_prefill_strerror.restype = ctypes.c_char_p
         lib.attn_prefill_strerror.argtypes = [ci]
         lib.attn_prefill_version.restype = ci
@@ -126,6 +131,20 @@ def decode_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, Lk, kv_capacity, n_q, n
         ctypes.c_void_p(out_ptr), ctypes.c_void_p(lse_ptr), int(B), int(Lk), int(kv_capacity),
         int(n_q), int(n_kv), int(d_h), float(scale), ctypes.c_void_p(ws_ptr), int(ws_bytes),
         ctypes.c_void_p(stream_ptr))
+
+
+def decode_noalloc_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, Lk, kv_capacity, n_q, n_kv,
+                       d_h, scale, stream_ptr):
+    """Direct call of attn_decode_fwd_noalloc with integer pointers; returns status."""
+    vp = ctypes.c_void_p
+    return library().attn_decode_fwd_noalloc(
+        vp(q_ptr), vp(k_ptr), vp(v_ptr), vp(out_ptr), vp(lse_ptr), int(B), int(Lk),
+        int(kv_capacity), int(n_q), int(n_kv), int(d_h), float(scale), vp(stream_ptr))
+
+
+def decode_scratch_bytes():
+    """Bytes of the static scratch attn_decode_fwd_noalloc runs on."""
+    return int(library().attn_decode_scratch_bytes())
 
 
 def decode_workspace_bytes(B, Lk, n_q, n_kv, d_h):

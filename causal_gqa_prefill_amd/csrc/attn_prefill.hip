@@ -73,6 +73,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "attn_prefill.h"
 #include "device_common.h"
@@ -1116,11 +1117,14 @@ extern "C" size_t attn_decode_workspace_bytes(int B, int Lk, int n_q, int n_kv, 
   return bytes;
 }
 
-extern "C" int attn_decode_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-                               int B, int Lk, long long kv_capacity, int n_q, int n_kv, int d_h,
-                               float scale, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream) {
-  if (!q || !k || !v || !out || !lse || !workspace) return ATTN_PREFILL_ERR_NULL_PTR;
+namespace {
+
+// Checks of a decode call's arguments other than the workspace; fills the
+// byte sizes of q/out, k/v and lse.
+int decode_check(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                 int B, int Lk, long long kv_capacity, int n_q, int n_kv, int d_h, float scale,
+                 size_t& qb, size_t& kvb, size_t& lb) {
+  if (!q || !k || !v || !out || !lse) return ATTN_PREFILL_ERR_NULL_PTR;
   if (B < 1 || Lk < 1 || n_q < 1 || n_kv < 1) return ATTN_PREFILL_ERR_BAD_SHAPE;
   if (kv_capacity < Lk) return ATTN_PREFILL_ERR_BAD_OFFSET;
   if (Lk > INT_MAX - 4096) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;  // key indices stay in int
@@ -1129,8 +1133,7 @@ extern "C" int attn_decode_fwd(const void* q, const void* k, const void* v, void
   if (d_h != 64 && d_h != 128) return ATTN_PREFILL_ERR_BAD_HEADDIM;
   if (!std::isfinite(scale)) return ATTN_PREFILL_ERR_BAD_SCALE;
   const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
-                          reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out) |
-                          reinterpret_cast<uintptr_t>(workspace);
+                          reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out);
   if ((align & 15) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3) != 0)
     return ATTN_PREFILL_ERR_MISALIGNED;
   size_t q_elems, kv_elems;
@@ -1141,21 +1144,27 @@ extern "C" int attn_decode_fwd(const void* q, const void* k, const void* v, void
       __builtin_mul_overflow(kv_elems, (size_t)d_h, &kv_elems) ||
       q_elems > ((size_t)1 << 61) || kv_elems > ((size_t)1 << 61))
     return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
-  const size_t need = attn_decode_workspace_bytes(B, Lk, n_q, n_kv, d_h);
-  if (need == 0) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
-  if (workspace_bytes < need) return ATTN_PREFILL_ERR_WORKSPACE;
+  const DecodeSplit sp = decode_split(B, Lk, n_kv);
+  if ((long long)B * n_kv * sp.n_split > INT_MAX || (long long)B * n_q > INT_MAX)
+    return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  qb = q_elems * 2;
+  kvb = kv_elems * 2;
+  lb = (size_t)B * n_q * 4;
+  if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kvb) || overlaps(out, qb, v, kvb) ||
+      overlaps(out, qb, lse, lb) || overlaps(lse, lb, q, qb) || overlaps(lse, lb, k, kvb) ||
+      overlaps(lse, lb, v, kvb))
+    return ATTN_PREFILL_ERR_ALIASING;
+  return ATTN_PREFILL_OK;
+}
+
+// The two decode kernels of a checked call on a workspace of at least
+// attn_decode_workspace_bytes() bytes.
+int decode_launch(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                  int Lk, long long kv_capacity, int n_q, int n_kv, int d_h, float scale,
+                  void* workspace, hipStream_t stream) {
   const DecodeSplit sp = decode_split(B, Lk, n_kv);
   const long long grid = (long long)B * n_kv * sp.n_split;
   const long long rows = (long long)B * n_q;
-  if (grid > INT_MAX || rows > INT_MAX) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
-  const size_t qb = q_elems * 2, kvb = kv_elems * 2, lb = (size_t)B * n_q * 4;
-  if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kvb) || overlaps(out, qb, v, kvb) ||
-      overlaps(out, qb, lse, lb) || overlaps(out, qb, workspace, need) ||
-      overlaps(lse, lb, q, qb) || overlaps(lse, lb, k, kvb) || overlaps(lse, lb, v, kvb) ||
-      overlaps(lse, lb, workspace, need) || overlaps(workspace, need, q, qb) ||
-      overlaps(workspace, need, k, kvb) || overlaps(workspace, need, v, kvb))
-    return ATTN_PREFILL_ERR_ALIASING;
-
   float* ws_o = static_cast<float*>(workspace);
   float* ws_lse = ws_o + (size_t)rows * sp.n_split * d_h;
   const unsigned short* qs = static_cast<const unsigned short*>(q);
@@ -1180,6 +1189,72 @@ extern "C" int attn_decode_fwd(const void* q, const void* k, const void* v, void
   return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
 }
 
+// Decode scratch for callers that cannot allocate: a static device array,
+// one copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address (on the host it names a stand-in, not device
+// memory): the device address of each GPU's copy is looked up once with
+// hipGetSymbolAddress, with that GPU current, and kept per device.
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch, or nullptr on failure.
+void* current_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int attn_decode_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                               int B, int Lk, long long kv_capacity, int n_q, int n_kv, int d_h,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  if (!workspace) return ATTN_PREFILL_ERR_NULL_PTR;
+  size_t qb = 0, kvb = 0, lb = 0;
+  const int st = decode_check(q, k, v, out, lse, B, Lk, kv_capacity, n_q, n_kv, d_h, scale, qb,
+                              kvb, lb);
+  if (st != ATTN_PREFILL_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0) return ATTN_PREFILL_ERR_MISALIGNED;
+  const size_t need = attn_decode_workspace_bytes(B, Lk, n_q, n_kv, d_h);
+  if (need == 0) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  if (workspace_bytes < need) return ATTN_PREFILL_ERR_WORKSPACE;
+  if (overlaps(out, qb, workspace, need) || overlaps(lse, lb, workspace, need) ||
+      overlaps(workspace, need, q, qb) || overlaps(workspace, need, k, kvb) ||
+      overlaps(workspace, need, v, kvb))
+    return ATTN_PREFILL_ERR_ALIASING;
+  return decode_launch(q, k, v, out, lse, B, Lk, kv_capacity, n_q, n_kv, d_h, scale, workspace,
+                       stream);
+}
+
+extern "C" size_t attn_decode_scratch_bytes(void) { return kDecodeScratchBytes; }
+
+extern "C" int attn_decode_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                                       float* lse, int B, int Lk, long long kv_capacity, int n_q,
+                                       int n_kv, int d_h, float scale, hipStream_t stream) {
+  size_t qb = 0, kvb = 0, lb = 0;
+  const int st = decode_check(q, k, v, out, lse, B, Lk, kv_capacity, n_q, n_kv, d_h, scale, qb,
+                              kvb, lb);
+  if (st != ATTN_PREFILL_OK) return st;
+  const size_t need = attn_decode_workspace_bytes(B, Lk, n_q, n_kv, d_h);
+  if (need == 0) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  if (need > kDecodeScratchBytes) return ATTN_PREFILL_ERR_SCRATCH;
+  void* ws = current_scratch();
+  if (ws == nullptr) return ATTN_PREFILL_ERR_LAUNCH;
+  return decode_launch(q, k, v, out, lse, B, Lk, kv_capacity, n_q, n_kv, d_h, scale, ws, stream);
+}
+
 extern "C" const char* attn_prefill_strerror(int status) {
   switch (status) {
     case ATTN_PREFILL_OK: return "success";
@@ -1200,6 +1275,9 @@ extern "C" const char* attn_prefill_strerror(int status) {
       return "decode supports at most 32 query heads per key/value head";
     case ATTN_PREFILL_ERR_WORKSPACE:
       return "workspace_bytes is smaller than attn_decode_workspace_bytes() for these sizes";
+    case ATTN_PREFILL_ERR_SCRATCH:
+      return "these sizes need more decode workspace than the static scratch holds "
+             "(attn_decode_scratch_bytes())";
     default: return "unknown status";
   }
 }

@@ -81,7 +81,9 @@ enum attn_prefill_status {
                                            kv_capacity < Lk                    */
     ATTN_PREFILL_ERR_UNSUPPORTED = 12,  /* (decode) more than 32 query heads
                                            per key/value head                  */
-    ATTN_PREFILL_ERR_WORKSPACE = 13     /* (decode) workspace_bytes too small  */
+    ATTN_PREFILL_ERR_WORKSPACE = 13,    /* (decode) workspace_bytes too small  */
+    ATTN_PREFILL_ERR_SCRATCH = 14       /* (decode, no allocation) the sizes
+                                           need more than the static scratch */
 };
 
 /*
@@ -235,6 +237,32 @@ int attn_decode_fwd(const void *q, const void *k, const void *v, void *out, floa
 /* Workspace bytes attn_decode_fwd needs for these sizes; 0 for sizes it
  * rejects (or whose workspace size overflows). */
 size_t attn_decode_workspace_bytes(int B, int Lk, int n_q, int n_kv, int d_h);
+
+/*
+ * attn_decode_fwd without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, layouts, numerics and
+ * errors as attn_decode_fwd minus the workspace; the same kernels run, on a
+ * static device scratch array of attn_decode_scratch_bytes() bytes (16 MiB)
+ * that the library holds on each GPU it runs on until the process ends.  Its
+ * device address is looked up on the first call on a device (with that device
+ * current); nothing is allocated, neither there nor on any call.
+ *   Sizes whose attn_decode_workspace_bytes() exceed the scratch return
+ *   ATTN_PREFILL_ERR_SCRATCH and enqueue nothing; a failed address lookup
+ *   returns ATTN_PREFILL_ERR_LAUNCH.
+ *   The scratch needs no initialisation (every partial is written before it
+ *   is read) and keeps the last call's partials afterwards.
+ *   Every call on one GPU shares that GPU's scratch: calls that may overlap
+ *   in time on one GPU (different streams, or different host threads without
+ *   ordering) race on it and must be ordered by the caller, e.g. by issuing
+ *   them on one stream.
+ */
+int attn_decode_fwd_noalloc(const void *q, const void *k, const void *v, void *out, float *lse,
+                            int B, int Lk, long long kv_capacity, int n_q, int n_kv, int d_h,
+                            float scale, hipStream_t stream);
+
+/* Bytes of the static scratch attn_decode_fwd_noalloc uses (16 MiB). */
+size_t attn_decode_scratch_bytes(void);
 
 /* Static text for a status code (never NULL). */
 const char *attn_prefill_strerror(int status);

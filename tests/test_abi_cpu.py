@@ -22,7 +22,8 @@ def _declared_functions():
 def test_library_exports_header_symbols():
     lib = binding.library()
     names = _declared_functions()
-    assert names == ["attn_decode_fwd", "attn_decode_workspace_bytes", "attn_merge_partials",
+    assert names == ["attn_decode_fwd", "attn_decode_fwd_noalloc", "attn_decode_scratch_bytes",
+                     "attn_decode_workspace_bytes", "attn_merge_partials",
                      "attn_prefill_bwd", "attn_prefill_fwd", "attn_prefill_fwd_chunk",
                      "attn_prefill_fwd_fp8", "attn_prefill_strerror", "attn_prefill_version"]
     for n in names:
@@ -31,7 +32,7 @@ def test_library_exports_header_symbols():
 
 def test_version_and_strerror():
     assert binding.library().attn_prefill_version() >= 300
-    for code in range(0, 14):
+    for code in range(0, 15):
         assert binding.strerror(code) not in ("", "unknown status")
     assert binding.strerror(99) == "unknown status"
 
@@ -167,6 +168,44 @@ def _call_decode(**kw):
 ])
 def test_decode_bad_arguments_rejected_on_host(kw, code):
     assert _call_decode(**kw) == code
+
+
+def _call_decode_noalloc(**kw):
+    args = dict(q=ALIGNED, k=ALIGNED + 0x10000000, v=ALIGNED + 0x20000000,
+                out=ALIGNED + 0x30000000, lse=ALIGNED + 0x40000000, B=2, Lk=100, cap=128,
+                n_q=8, n_kv=2, d_h=128, scale=0.125, stream=0)
+    args.update(kw)
+    return binding.decode_noalloc_raw(args["q"], args["k"], args["v"], args["out"], args["lse"],
+                                      args["B"], args["Lk"], args["cap"], args["n_q"],
+                                      args["n_kv"], args["d_h"], args["scale"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(lse=0), 1),
+    (dict(B=0), 2), (dict(Lk=0), 2),
+    (dict(n_q=7), 3), (dict(n_q=66), 12), (dict(d_h=80), 4), (dict(scale=float("nan")), 5),
+    (dict(cap=99), 11), (dict(lse=ALIGNED + 0x40000002), 7),
+    (dict(out=ALIGNED + 0x10000000 + 512), 9),
+])
+def test_decode_noalloc_bad_arguments_rejected_on_host(kw, code):
+    assert _call_decode_noalloc(**kw) == code
+
+
+def test_decode_noalloc_scratch_limit():
+    """Sizes whose workspace exceeds the static scratch are refused before any
+    HIP call (the buffers sit far apart so that nothing else fails first)."""
+    limit = binding.decode_scratch_bytes()
+    assert limit == 16 << 20
+    big = (2048, 4096, 64, 8, 128)
+    assert binding.decode_workspace_bytes(*big) > limit
+    B, Lk, n_q, n_kv, d = big
+    far = 1 << 40
+    assert _call_decode_noalloc(q=ALIGNED, k=ALIGNED + far, v=ALIGNED + 2 * far,
+                                out=ALIGNED + 3 * far, lse=ALIGNED + 4 * far, B=B, Lk=Lk, cap=Lk,
+                                n_q=n_q, n_kv=n_kv, d_h=d) == 14
+    # the largest decode workloads fit
+    for sizes in ((32, 8192, 32, 8, 128), (1, 131072, 36, 6, 128), (8, 32768, 64, 8, 128)):
+        assert 0 < binding.decode_workspace_bytes(*sizes) <= limit
 
 
 def _call_fp8(**kw):
