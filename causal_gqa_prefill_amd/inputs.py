@@ -52,26 +52,31 @@ def _e4m3_positive_values():
 
 def e4m3_bits(x) -> np.ndarray:
     """float32 array -> OCP e4m3 codes (uint8), round to nearest, ties to the
-    even code.  |x| must not exceed 464 (the largest finite code's range)."""
+    even code.  |x| must not exceed 464 (the largest finite code's range).
+
+    Normal range (|x| >= 2^-6): the float32 significand is rounded to 3 bits
+    (nearest even) by integer arithmetic on the bit pattern, and the exponent
+    re-biased from 127 to 7.  Below 2^-6 the codes are the subnormals
+    m * 2^-9, m = |x| * 512 rounded to nearest even (m = 8 is the smallest
+    normal, whose code is 8 as well).  Values in [448, 464] map to 448."""
     x = np.asarray(x, dtype=np.float32)
     flat = x.reshape(-1)
     out = np.empty(flat.shape, dtype=np.uint8)
-    # float32 holds every e4m3 value, and the two differences below are exact
-    # (neighbouring codes are within a factor 2 of each other, or zero)
-    table = _e4m3_positive_values().astype(np.float32)
     step = 1 << 22   # bounded temporaries for tensors of hundreds of millions of values
     for i0 in range(0, flat.size, step):
         xs = flat[i0:i0 + step]
         a = np.abs(xs)
         if np.any(a > 464.0) or not np.all(np.isfinite(a)):
             raise ValueError("values outside the e4m3 range")
-        hi = np.clip(np.searchsorted(table, a), 1, 126)
-        lo = hi - 1
-        dlo = a - table[lo]
-        dhi = table[hi] - a
-        pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
-        code = np.where(pick_hi, hi, lo).astype(np.uint8)
-        code[a >= table[126]] = 126
+        u = a.view(np.uint32)
+        # nearest-even rounding of the significand to 3 bits (carry may bump the exponent)
+        r = u + np.uint32(0x7FFFF) + ((u >> np.uint32(20)) & np.uint32(1))
+        exp = (r >> np.uint32(23)).astype(np.int32) - 127 + 7
+        normal = ((exp << 3) | ((r >> np.uint32(20)) & np.uint32(7)).astype(np.int32))
+        sub = np.rint(a * np.float32(512.0)).astype(np.int32)   # exact scaling, then RNE
+        code = np.where(a >= np.float32(2.0 ** -6), normal, sub)
+        code = np.minimum(code, 126)
+        code = code.astype(np.uint8)
         code[np.signbit(xs)] |= np.uint8(0x80)
         out[i0:i0 + step] = code
     return out.reshape(x.shape)

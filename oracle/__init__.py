@@ -52,7 +52,7 @@ def load_library(path):
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
         ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int,
         ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
-        dp, dp, dp, ctypes.POINTER(ctypes.c_uint64), ctypes.c_int,
+        dp, dp, ctypes.POINTER(ctypes.c_uint64), ctypes.c_int,
     ]
     lib.oracle_e4m3_table.restype = None
     lib.oracle_e4m3_table.argtypes = [dp]
@@ -60,17 +60,18 @@ def load_library(path):
     lib.oracle_attn_bwd_rowstats.restype = ctypes.c_int
     lib.oracle_attn_bwd_rowstats.argtypes = [
         u16p, u16p, u16p, u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, dp, ctypes.c_int]
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, i64p, ctypes.c_int64,
+        dp, dp, dp, ctypes.c_int]
     lib.oracle_attn_bwd_dq.restype = ctypes.c_int
     lib.oracle_attn_bwd_dq.argtypes = [
         u16p, u16p, u16p, u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, dp, i64p,
-        ctypes.c_int64, dp, dp, ctypes.c_int]
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, i64p,
+        ctypes.c_int64, dp, ctypes.c_int]
     lib.oracle_attn_bwd_dkdv.restype = ctypes.c_int
     lib.oracle_attn_bwd_dkdv.argtypes = [
         u16p, u16p, u16p, u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, dp, i64p,
-        ctypes.c_int64, dp, dp, dp, dp, ctypes.c_int]
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int, dp, dp, i64p,
+        ctypes.c_int64, dp, dp, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_version.restype = ctypes.c_int
     return lib
@@ -224,10 +225,7 @@ def attention_rows_chunk_fp8(q, k, v, scale, descale_q, descale_k, descale_v, ca
     exactly, times their fp32 descale factors, then the plain fp64 attention.
 
     q: uint8 [B, n_q, Lq, d_h]; k, v: uint8 [B, n_kv, Lk, d_h] (e4m3 codes).
-    Returns (out [n_rows, d_h], lse [n_rows], bound [n_rows, d_h], flops):
-    bound is, per element, 2^-4 sum_j P_j |v_j| + 2^-10 max_j P_j sum_j |v_j|
-    over the visible keys, the most that rounding the weights to e4m3 can
-    move that element of out.
+    Returns (out [n_rows, d_h], lse [n_rows], flops).
     """
     if q.ndim != 4 or k.ndim != 4:
         raise ValueError("q, k, v must be 4-D [B, heads, L, d_h]")
@@ -247,7 +245,6 @@ def attention_rows_chunk_fp8(q, k, v, scale, descale_q, descale_k, descale_v, ca
         rows_p = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
     out = np.empty((n_rows, d_h), dtype=np.float64)
     lse = np.empty((n_rows,), dtype=np.float64)
-    bound = np.empty((n_rows, d_h), dtype=np.float64)
     flops = ctypes.c_uint64(0)
     u8p = ctypes.POINTER(ctypes.c_uint8)
     dp = ctypes.POINTER(ctypes.c_double)
@@ -256,11 +253,10 @@ def attention_rows_chunk_fp8(q, k, v, scale, descale_q, descale_k, descale_v, ca
         B, Lq, Lk, int(q_offset), n_q, n_kv, d_h, float(np.float32(scale)),
         float(np.float32(descale_q)), float(np.float32(descale_k)),
         float(np.float32(descale_v)), int(causal), rows_p, n_rows,
-        out.ctypes.data_as(dp), lse.ctypes.data_as(dp), bound.ctypes.data_as(dp),
-        ctypes.byref(flops), int(threads))
+        out.ctypes.data_as(dp), lse.ctypes.data_as(dp), ctypes.byref(flops), int(threads))
     if rc != OK:
         raise ValueError(f"oracle_attn_rows_chunk_fp8 failed with code {rc}")
-    return out, lse, bound, int(flops.value)
+    return out, lse, int(flops.value)
 
 
 # ---------------------------------------------------------------------------
@@ -286,71 +282,74 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def attention_bwd_rowstats(q, k, v, dout, scale, causal=True, threads=0, lib=None):
-    """Every row's LSE, delta = dO . O (exact O) and sum_t |dO_t O_t|, fp64
-    [B * n_q * L] each."""
+def attention_bwd_rowstats(q, k, v, dout, scale, causal=True, rows=None, threads=0, lib=None):
+    """Row statistics of the backward pass for flat query rows
+    (b * n_q + h) * L + i (None: every row): (out [n, d_h], lse [n],
+    delta [n]) with out the exact attention output and delta = dO . out,
+    fp64."""
     q, k, v, dout, B, n_q, n_kv, L, d = _bwd_shapes(q, k, v, dout)
-    lse = np.empty(B * n_q * L)
-    delta = np.empty(B * n_q * L)
-    absd = np.empty(B * n_q * L)
+    if rows is None:
+        n = B * n_q * L
+        rows_p = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n = int(rows.size)
+        rows_p = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    out = np.empty((n, d))
+    lse = np.empty(n)
+    delta = np.empty(n)
     u16p = ctypes.POINTER(ctypes.c_uint16)
     rc = (lib or _load()).oracle_attn_bwd_rowstats(
         q.ctypes.data_as(u16p), k.ctypes.data_as(u16p), v.ctypes.data_as(u16p),
         dout.ctypes.data_as(u16p), B, L, n_q, n_kv, d, float(np.float32(scale)), int(causal),
-        _ptr(lse), _ptr(delta), _ptr(absd), int(threads))
+        rows_p, n, _ptr(out), _ptr(lse), _ptr(delta), int(threads))
     if rc != OK:
         raise ValueError(f"oracle_attn_bwd_rowstats failed with code {rc}")
-    return lse, delta, absd
+    return out, lse, delta
 
 
-def attention_bwd_dq(q, k, v, dout, scale, causal, lse, delta, rows, abs_delta=None,
-                     threads=0, lib=None):
-    """dQ [len(rows), d_h] for flat query rows (b * n_q + h) * L + i; with
-    abs_delta given also the per-element rounding bound (see the C source):
-    returns dq or (dq, bound)."""
+def attention_bwd_dq(q, k, v, dout, scale, causal, lse, delta, rows, threads=0, lib=None):
+    """dQ [len(rows), d_h] for flat query rows (b * n_q + h) * L + i; lse and
+    delta indexed by flat row (only the requested rows are read)."""
     q, k, v, dout, B, n_q, n_kv, L, d = _bwd_shapes(q, k, v, dout)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     lse = np.ascontiguousarray(lse, dtype=np.float64)
     delta = np.ascontiguousarray(delta, dtype=np.float64)
-    absd = None if abs_delta is None else np.ascontiguousarray(abs_delta, dtype=np.float64)
+    if lse.size != B * n_q * L or delta.size != B * n_q * L:
+        raise ValueError("lse and delta must hold one entry per query row")
     out = np.empty((rows.size, d))
-    bound = None if absd is None else np.empty((rows.size, d))
     u16p = ctypes.POINTER(ctypes.c_uint16)
     rc = (lib or _load()).oracle_attn_bwd_dq(
         q.ctypes.data_as(u16p), k.ctypes.data_as(u16p), v.ctypes.data_as(u16p),
         dout.ctypes.data_as(u16p), B, L, n_q, n_kv, d, float(np.float32(scale)), int(causal),
-        _ptr(lse), _ptr(delta), _ptr(absd),
-        rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size,
-        _ptr(out), _ptr(bound), int(threads))
+        _ptr(lse), _ptr(delta), rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size,
+        _ptr(out), int(threads))
     if rc != OK:
         raise ValueError(f"oracle_attn_bwd_dq failed with code {rc}")
-    return out if bound is None else (out, bound)
+    return out
 
 
-def attention_bwd_dkdv(q, k, v, dout, scale, causal, lse, delta, rows, abs_delta=None,
-                       threads=0, lib=None):
+def attention_bwd_dkdv(q, k, v, dout, scale, causal, lse, delta, rows, threads=0, lib=None):
     """(dK, dV) [len(rows), d_h] for flat key rows (b * n_kv + kvh) * L + j;
-    with abs_delta given also their rounding bounds: (dk, dv, bound_dk,
-    bound_dv)."""
+    lse and delta indexed by flat query row (the rows that see a requested
+    key are read)."""
     q, k, v, dout, B, n_q, n_kv, L, d = _bwd_shapes(q, k, v, dout)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     lse = np.ascontiguousarray(lse, dtype=np.float64)
     delta = np.ascontiguousarray(delta, dtype=np.float64)
-    absd = None if abs_delta is None else np.ascontiguousarray(abs_delta, dtype=np.float64)
+    if lse.size != B * n_q * L or delta.size != B * n_q * L:
+        raise ValueError("lse and delta must hold one entry per query row")
     dk = np.empty((rows.size, d))
     dv = np.empty((rows.size, d))
-    bk = None if absd is None else np.empty((rows.size, d))
-    bv = None if absd is None else np.empty((rows.size, d))
     u16p = ctypes.POINTER(ctypes.c_uint16)
     rc = (lib or _load()).oracle_attn_bwd_dkdv(
         q.ctypes.data_as(u16p), k.ctypes.data_as(u16p), v.ctypes.data_as(u16p),
         dout.ctypes.data_as(u16p), B, L, n_q, n_kv, d, float(np.float32(scale)), int(causal),
-        _ptr(lse), _ptr(delta), _ptr(absd),
-        rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size,
-        _ptr(dk), _ptr(dv), _ptr(bk), _ptr(bv), int(threads))
+        _ptr(lse), _ptr(delta), rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size,
+        _ptr(dk), _ptr(dv), int(threads))
     if rc != OK:
         raise ValueError(f"oracle_attn_bwd_dkdv failed with code {rc}")
-    return (dk, dv) if bk is None else (dk, dv, bk, bv)
+    return dk, dv
 
 
 def attention_bwd(q, k, v, dout, scale, causal=True, threads=0, lib=None):
@@ -358,7 +357,8 @@ def attention_bwd(q, k, v, dout, scale, causal=True, threads=0, lib=None):
     plus the row statistics (lse, delta)."""
     B, n_q, L, d = q.shape
     n_kv = k.shape[1]
-    lse, delta, _ = attention_bwd_rowstats(q, k, v, dout, scale, causal, threads, lib)
+    _, lse, delta = attention_bwd_rowstats(q, k, v, dout, scale, causal, threads=threads,
+                                           lib=lib)
     dq = attention_bwd_dq(q, k, v, dout, scale, causal, lse, delta,
                           np.arange(B * n_q * L), threads=threads, lib=lib)
     dk, dv = attention_bwd_dkdv(q, k, v, dout, scale, causal, lse, delta,

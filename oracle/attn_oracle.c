@@ -39,9 +39,7 @@
  * attention): q, k, v may instead be OCP e4m3 codes with an fp32 descale
  * factor each; the oracle decodes every code exactly (sign, 4 exponent bits
  * with bias 7, 3 mantissa bits, subnormals below 2^-6, S.1111.111 = NaN),
- * multiplies by the descale in fp64 and runs the same plain attention.  For
- * that path it also returns, per output element, the bound that rounding
- * the weights to e4m3 can move it by (see oracle_attn_rows_chunk_fp8).
+ * multiplies by the descale in fp64 and runs the same plain attention.
  *
  * Layouts: q [B, n_q, Lq, d_h], k and v [B, n_kv, Lk, d_h], bf16 bit
  * patterns (uint16) or e4m3 codes (uint8), row-major, d_h fastest.  A "row"
@@ -63,7 +61,7 @@
 #define ORACLE_BAD_ARG 1
 #define ORACLE_NO_MEMORY 2
 
-int oracle_version(void) { return 3; }
+int oracle_version(void) { return 4; }
 
 /* A bf16 bit pattern is the upper half of an fp32 bit pattern, so widening is
  * exact: shift into place, reinterpret as float, convert to double. */
@@ -105,16 +103,12 @@ static inline double elem(int kind, const void *base, int64_t idx, double mul)
 }
 
 /* One query row, done the plain way.  s and w are scratch rows of length Lk.
- * dq, dk, dv multiply the decoded q, k, v (1 for bf16).  bound, if not NULL,
- * receives per output element 2^-4 sum_j P_j |v_j| + 2^-10 max_j P_j
- * sum_j |v_j| over the visible keys: the most that rounding each weight to
- * e4m3 (relative error <= 2^-4 in the normal range, absolute <= 2^-10 of
- * the reference max below it) can move the element. */
+ * dq, dk, dv multiply the decoded q, k, v (1 for bf16). */
 static void one_row(int kind, const void *q, const void *k, const void *v,
                     int64_t Lq, int64_t Lk, int64_t q_off, int64_t n_q,
                     int64_t n_kv, int64_t d_h, double scale, double dq, double dk,
                     double dv, int causal, int64_t row, double *s, double *w,
-                    double *out, double *lse, double *bound, uint64_t *flops)
+                    double *out, double *lse, uint64_t *flops)
 {
     const int64_t L = Lk;
     const int64_t g = n_q / n_kv;
@@ -163,21 +157,6 @@ static void one_row(int kind, const void *q, const void *k, const void *v,
         for (int64_t t = 0; t < d_h; ++t)
             out[t] += p * elem(kind, v, vrow + t, dv);
     }
-    /* 5b. the e4m3 weight-rounding bound per element */
-    if (bound) {
-        double p_max = 0.0;
-        for (int64_t j = 0; j < n_vis; ++j)
-            if (w[j] > p_max) p_max = w[j];
-        for (int64_t t = 0; t < d_h; ++t) {
-            double weighted = 0.0, plain = 0.0;
-            for (int64_t j = 0; j < n_vis; ++j) {
-                const double a = fabs(elem(kind, v, vbase + j * d_h + t, dv));
-                weighted += w[j] * a;
-                plain += a;
-            }
-            bound[t] = ldexp(weighted, -4) + ldexp(p_max * plain, -10);
-        }
-    }
     /* 6. saved row statistic: natural-log log-sum-exp of the scaled scores */
     *lse = m + log(total);
     /* 2*d_h flops per visible pair for Q K^T and 2*d_h for P V */
@@ -198,8 +177,7 @@ static int rows_generic(int kind, const void *q, const void *k, const void *v,
                         int64_t n_q, int64_t n_kv, int64_t d_h, float scale,
                         double dq, double dk, double dv,
                         int causal, const int64_t *rows, int64_t n_rows,
-                        double *out, double *lse, double *bound, uint64_t *flops,
-                        int threads)
+                        double *out, double *lse, uint64_t *flops, int threads)
 {
     if (!q || !k || !v || !out || !lse || !flops) return ORACLE_BAD_ARG;
     if (B < 1 || Lq < 1 || Lk < 1 || n_q < 1 || n_kv < 1 || d_h < 1) return ORACLE_BAD_ARG;
@@ -235,8 +213,7 @@ static int rows_generic(int kind, const void *q, const void *k, const void *v,
             }
             const int64_t row = rows ? rows[r] : r;
             one_row(kind, q, k, v, Lq, Lk, q_off, n_q, n_kv, d_h, sc, dq, dk, dv, causal,
-                    row, s, w, out + r * d_h, lse + r, bound ? bound + r * d_h : NULL,
-                    &count);
+                    row, s, w, out + r * d_h, lse + r, &count);
         }
         free(s);
         free(w);
@@ -252,29 +229,26 @@ int oracle_attn_rows_chunk(const uint16_t *q, const uint16_t *k, const uint16_t 
                            double *out, double *lse, uint64_t *flops, int threads)
 {
     return rows_generic(KIND_BF16, q, k, v, B, Lq, Lk, q_off, n_q, n_kv, d_h, scale,
-                        1.0, 1.0, 1.0, causal, rows, n_rows, out, lse, NULL, flops, threads);
+                        1.0, 1.0, 1.0, causal, rows, n_rows, out, lse, flops, threads);
 }
 
 /*
  * The chunk with e4m3 inputs: q, k, v are OCP e4m3 codes, decoded exactly
  * and multiplied by descale_q, descale_k, descale_v (fp32 values, widened
- * exactly).  Arguments and results otherwise as oracle_attn_rows_chunk;
- * bound (NULL or [n_rows, d_h]) receives the per-element weight-rounding
- * bound described at one_row.
+ * exactly).  Arguments and results otherwise as oracle_attn_rows_chunk.
  */
 int oracle_attn_rows_chunk_fp8(const uint8_t *q, const uint8_t *k, const uint8_t *v,
                                int64_t B, int64_t Lq, int64_t Lk, int64_t q_off,
                                int64_t n_q, int64_t n_kv, int64_t d_h, float scale,
                                float descale_q, float descale_k, float descale_v,
                                int causal, const int64_t *rows, int64_t n_rows,
-                               double *out, double *lse, double *bound, uint64_t *flops,
-                               int threads)
+                               double *out, double *lse, uint64_t *flops, int threads)
 {
     if (!isfinite(descale_q) || !isfinite(descale_k) || !isfinite(descale_v))
         return ORACLE_BAD_ARG;
     return rows_generic(KIND_E4M3, q, k, v, B, Lq, Lk, q_off, n_q, n_kv, d_h, scale,
                         (double)descale_q, (double)descale_k, (double)descale_v, causal,
-                        rows, n_rows, out, lse, bound, flops, threads);
+                        rows, n_rows, out, lse, flops, threads);
 }
 
 /* Decoded value of every e4m3 code (for pinning the decoder): out[256]. */
@@ -312,34 +286,36 @@ int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  * Whole sequences only (Lq = Lk = L, query i sees j <= i when causal).
  * ------------------------------------------------------------------------ */
 
-/* Per-row statistics for the backward pass: lse[r] (natural log, as the
- * forward oracle) and delta[r] = sum_t dO[r,t] O[r,t] with O the exact
- * output, for every row r, in fp64; abs_delta (NULL or [rows]) receives
- * sum_t |dO[r,t] O[r,t]|. */
+/* Per-row statistics for the backward pass, for the requested query rows
+ * (flat (b * n_q + h) * L + i; rows == NULL: every row, n_rows = B n_q L):
+ * lse[r] (natural log, as the forward oracle) and delta[r] = sum_t dO[r,t]
+ * O[r,t] with O the exact output, in fp64; out (NULL or [n_rows, d_h])
+ * receives that output. */
 int oracle_attn_bwd_rowstats(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                              const uint16_t *dout, int64_t B, int64_t L, int64_t n_q,
                              int64_t n_kv, int64_t d_h, float scale, int causal,
-                             double *lse, double *delta, double *abs_delta, int threads)
+                             const int64_t *rows, int64_t n_rows, double *out, double *lse,
+                             double *delta, int threads)
 {
     if (!dout || !delta) return ORACLE_BAD_ARG;
-    const int64_t n_rows = B * n_q * L;
-    double *o = (double *)malloc((size_t)n_rows * (size_t)d_h * sizeof(double));
-    if (!o) return ORACLE_NO_MEMORY;
+    double *o = out;
+    if (!o) {
+        o = (double *)malloc((size_t)n_rows * (size_t)d_h * sizeof(double));
+        if (!o) return ORACLE_NO_MEMORY;
+    }
     uint64_t flops = 0;
     int rc = rows_generic(KIND_BF16, q, k, v, B, L, L, 0, n_q, n_kv, d_h, scale, 1.0, 1.0, 1.0,
-                          causal, NULL, n_rows, o, lse, NULL, &flops, threads);
+                          causal, rows, n_rows, o, lse, &flops, threads);
     if (rc == ORACLE_OK) {
         for (int64_t r = 0; r < n_rows; ++r) {
-            double acc = 0.0, mag = 0.0;
-            for (int64_t t = 0; t < d_h; ++t) {
-                acc += widen_bf16(dout[r * d_h + t]) * o[r * d_h + t];
-                mag += fabs(widen_bf16(dout[r * d_h + t]) * o[r * d_h + t]);
-            }
+            const int64_t row = rows ? rows[r] : r;
+            double acc = 0.0;
+            for (int64_t t = 0; t < d_h; ++t)
+                acc += widen_bf16(dout[row * d_h + t]) * o[r * d_h + t];
             delta[r] = acc;
-            if (abs_delta) abs_delta[r] = mag;
         }
     }
-    free(o);
+    if (o != out) free(o);
     return rc;
 }
 
@@ -372,47 +348,15 @@ static double bwd_dp(const uint16_t *v, const uint16_t *dout, int64_t L, int64_t
     return acc;
 }
 
-/* Rounding bounds for a kernel that recomputes P in fp32 from an fp32 LSE,
- * accumulates products of bf16 values in fp32, forms D from O rounded to
- * bf16, rounds P and dS to bf16 (nearest even) for the products and the
- * gradients to bf16 once:
- *   u = 2^-8 (bf16's unit roundoff: 8 significant bits, nearest even),
- *   eP = 2^-16 (relative error of the fp32 P),
- *   ea = 2^-16 (an fp32 sum of up to 256 products: 256 x 2^-24),
- *   E_ij = (u + eP) |dS_ij| + P_ij (ea sum_t |dO_it v_jt| + (u + ea) A_i),
- *   A_i = sum_t |dO_it O_it|,
- *   |dV_jt error| <= (u + eP + ea) sum_i P_ij |dO_it| + u |dV_jt|,
- *   |dQ_it error| <= scale sum_j (E_ij + ea |dS_ij|) |k_jt| + u |dQ_it|,
- *   |dK_jt error| <= scale sum_i (E_ij + ea |dS_ij|) |q_it| + u |dK_jt|. */
-static const double BWD_U = 1.0 / 256.0;
-static const double BWD_EP = 1.0 / 65536.0;
-static const double BWD_EA = 1.0 / 65536.0;
-
-/* sum_t |dO_it v_jt| */
-static double bwd_abs_dp(const uint16_t *v, const uint16_t *dout, int64_t L, int64_t n_q,
-                         int64_t n_kv, int64_t d_h, int64_t b, int64_t h, int64_t i, int64_t j)
-{
-    const int64_t kvh = h / (n_q / n_kv);
-    const uint16_t *drow = dout + ((b * n_q + h) * L + i) * d_h;
-    const uint16_t *vrow = v + ((b * n_kv + kvh) * L + j) * d_h;
-    double acc = 0.0;
-    for (int64_t t = 0; t < d_h; ++t)
-        acc += fabs(widen_bf16(drow[t]) * widen_bf16(vrow[t]));
-    return acc;
-}
-
 /* dQ for the requested query rows (flat (b * n_q + h) * L + i):
- * dq [n_rows, d_h] fp64.  lse and delta: every row's statistics, from
- * oracle_attn_bwd_rowstats.  bound (NULL or [n_rows, d_h], then abs_delta
- * from oracle_attn_bwd_rowstats is required) receives the rounding bound
- * described above. */
+ * dq [n_rows, d_h] fp64.  lse and delta: every row's statistics (indexed by
+ * flat row; only the requested rows' entries are read). */
 int oracle_attn_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                        const uint16_t *dout, int64_t B, int64_t L, int64_t n_q, int64_t n_kv,
                        int64_t d_h, float scale, int causal, const double *lse,
-                       const double *delta, const double *abs_delta, const int64_t *rows,
-                       int64_t n_rows, double *dq, double *bound, int threads)
+                       const double *delta, const int64_t *rows, int64_t n_rows, double *dq,
+                       int threads)
 {
-    if (bound && !abs_delta) return ORACLE_BAD_ARG;
     if (!q || !k || !v || !dout || !lse || !delta || !rows || !dq) return ORACLE_BAD_ARG;
     if (B < 1 || L < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || n_q % n_kv) return ORACLE_BAD_ARG;
     for (int64_t r = 0; r < n_rows; ++r)
@@ -429,40 +373,28 @@ int oracle_attn_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         const int64_t i = row % L, h = (row / L) % n_q, b = row / (L * n_q);
         const int64_t kvh = h / (n_q / n_kv);
         double *out = dq + r * d_h;
-        double *bnd = bound ? bound + r * d_h : NULL;
         for (int64_t t = 0; t < d_h; ++t) out[t] = 0.0;
-        if (bnd)
-            for (int64_t t = 0; t < d_h; ++t) bnd[t] = 0.0;
         const int64_t n_vis = causal ? i + 1 : L;
         for (int64_t j = 0; j < n_vis; ++j) {
             const double p = bwd_weight(q, k, L, n_q, n_kv, d_h, sc, causal, b, h, i, j, lse[row]);
             const double ds = p * (bwd_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j) - delta[row]);
             const uint16_t *krow = k + ((b * n_kv + kvh) * L + j) * d_h;
             for (int64_t t = 0; t < d_h; ++t) out[t] += sc * ds * widen_bf16(krow[t]);
-            if (bnd) {
-                const double e = (BWD_U + BWD_EP + BWD_EA) * fabs(ds) +
-                                 p * (BWD_EA * bwd_abs_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j) +
-                                      (BWD_U + BWD_EA) * abs_delta[row]);
-                for (int64_t t = 0; t < d_h; ++t) bnd[t] += sc * e * fabs(widen_bf16(krow[t]));
-            }
         }
-        if (bnd)
-            for (int64_t t = 0; t < d_h; ++t) bnd[t] += BWD_U * fabs(out[t]);
     }
     return ORACLE_OK;
 }
 
 /* dK and dV for the requested key rows (flat (b * n_kv + kvh) * L + j):
  * dk, dv [n_rows, d_h] fp64, summed over the g query heads of the group and
- * every query row that sees key j. */
+ * every query row that sees key j.  lse and delta as for oracle_attn_bwd_dq;
+ * the entries of the query rows that see a requested key are read. */
 int oracle_attn_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const uint16_t *dout, int64_t B, int64_t L, int64_t n_q, int64_t n_kv,
                          int64_t d_h, float scale, int causal, const double *lse,
-                         const double *delta, const double *abs_delta, const int64_t *rows,
-                         int64_t n_rows, double *dk, double *dv, double *bound_dk,
-                         double *bound_dv, int threads)
+                         const double *delta, const int64_t *rows, int64_t n_rows, double *dk,
+                         double *dv, int threads)
 {
-    if ((bound_dk || bound_dv) && !(bound_dk && bound_dv && abs_delta)) return ORACLE_BAD_ARG;
     if (!q || !k || !v || !dout || !lse || !delta || !rows || !dk || !dv) return ORACLE_BAD_ARG;
     if (B < 1 || L < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || n_q % n_kv) return ORACLE_BAD_ARG;
     for (int64_t r = 0; r < n_rows; ++r)
@@ -479,11 +411,7 @@ int oracle_attn_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v
         const int64_t row = rows[r];
         const int64_t j = row % L, kvh = (row / L) % n_kv, b = row / (L * n_kv);
         double *ok = dk + r * d_h, *ov = dv + r * d_h;
-        double *bk = bound_dk ? bound_dk + r * d_h : NULL;
-        double *bv = bound_dv ? bound_dv + r * d_h : NULL;
         for (int64_t t = 0; t < d_h; ++t) ok[t] = ov[t] = 0.0;
-        if (bk)
-            for (int64_t t = 0; t < d_h; ++t) bk[t] = bv[t] = 0.0;
         for (int64_t h = kvh * g; h < kvh * g + g; ++h) {
             for (int64_t i = causal ? j : 0; i < L; ++i) {
                 const int64_t qrow_id = (b * n_q + h) * L + i;
@@ -497,23 +425,8 @@ int oracle_attn_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v
                     ov[t] += p * widen_bf16(drow[t]);
                     ok[t] += sc * ds * widen_bf16(qrow[t]);
                 }
-                if (bk) {
-                    const double e =
-                        (BWD_U + BWD_EP + BWD_EA) * fabs(ds) +
-                        p * (BWD_EA * bwd_abs_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j) +
-                             (BWD_U + BWD_EA) * abs_delta[qrow_id]);
-                    for (int64_t t = 0; t < d_h; ++t) {
-                        bk[t] += sc * e * fabs(widen_bf16(qrow[t]));
-                        bv[t] += (BWD_U + BWD_EP + BWD_EA) * p * fabs(widen_bf16(drow[t]));
-                    }
-                }
             }
         }
-        if (bk)
-            for (int64_t t = 0; t < d_h; ++t) {
-                bk[t] += BWD_U * fabs(ok[t]);
-                bv[t] += BWD_U * fabs(ov[t]);
-            }
     }
     return ORACLE_OK;
 }

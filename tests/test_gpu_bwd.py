@@ -3,15 +3,18 @@ through the C ABI ("Long-Context Attention Explained", section "What
 FlashAttention does not change": gradients recomputed from the saved LSE).
 
 The kernels receive the oracle's output rounded to bf16 and its LSE rounded
-to fp32, so the comparison isolates the backward arithmetic.  Contract: every
-element of dQ, dK and dV within the oracle's per-element rounding bound (P
+to fp32 for every query row the checked gradients depend on, so the
+comparison isolates the backward arithmetic.  Contract: every checked element
+of dQ, dK and dV within the per-element rounding bound of tests/bounds.py (P
 recomputed in fp32, delta from the bf16 output, P and dS rounded to bf16,
-fp32 accumulation, one bf16 rounding of the result; pinned on the CPU by a
-simulation), delta within its own bound.
+fp32 sums charged one rounding per term over their true lengths, one bf16
+rounding of the result; pinned on the CPU by a simulation that accumulates
+in fp32), delta within its own bound.
 """
 import numpy as np
 import pytest
 
+import bounds
 import oracle
 from causal_gqa_prefill_amd import inputs
 from causal_gqa_prefill_amd.configs import config
@@ -39,40 +42,82 @@ def _check(name, got, ref, bound):
     assert np.all(err <= bound + 1e-7), f"{name}: {np.sum(err > bound + 1e-7)} past the bound"
 
 
-def _run_case(B, L, n_q, n_kv, d, causal, seed, q_rows=None, k_rows=None, label=""):
-    """Oracle stats and outputs for (all or sampled) rows, GPU backward with the
-    oracle's O (bf16) and LSE (fp32), compare."""
+def _run_case(B, L, n_q, n_kv, d, causal, seed, q_rows=None, k_rows=None, label="",
+              groups=None):
+    """Oracle statistics of the query rows the checked gradients depend on,
+    GPU backward fed the oracle's O (bf16) and LSE (fp32) for those rows (the
+    other rows hold O = 0, LSE = 0: finite, never read by a checked
+    gradient), then dQ on q_rows and dK, dV on k_rows (flat ids; None: every
+    row of the checked groups) against the oracle within the bounds.
+    groups: (b, kv-head) pairs to check (None: all)."""
     import torch
     from causal_gqa_prefill_amd import attn_prefill_backward
     scale = float(np.float32(d ** -0.5))
+    g = n_q // n_kv
     q, k, v = inputs.make_qkv(B, L, n_q, n_kv, d, seed)
     do = inputs.make_qkv(B, L, n_q, n_kv, d, seed + 500)[0]
     name = label or f"bwd B={B} L={L} n_q={n_q} n_kv={n_kv} causal={causal}"
     say(f"case {name}")
-    o, lse_o, _ = oracle.attention_rows(q, k, v, scale, causal)
-    lse, delta, absd = oracle.attention_bwd_rowstats(q, k, v, do, scale, causal)
-    o_bits = inputs.bf16_bits(o.astype(np.float32)).reshape(q.shape)
+    if groups is None:
+        groups = [(b, h) for b in range(B) for h in range(n_kv)]
+    if q_rows is None:
+        q_rows = np.concatenate([((b * n_q + kvh * g + hh) * L + np.arange(L))
+                                 for b, kvh in groups for hh in range(g)])
+    if k_rows is None:
+        k_rows = np.concatenate([((b * n_kv + kvh) * L + np.arange(L)) for b, kvh in groups])
+    q_rows, k_rows = np.asarray(q_rows), np.asarray(k_rows)
+    # query rows the checked gradients read: the dQ rows, and every row of
+    # the group that sees a checked key
+    parts = [q_rows]
+    kb, kh, kj = k_rows // (n_kv * L), (k_rows // L) % n_kv, k_rows % L
+    for b, kvh in {(int(x), int(y)) for x, y in zip(kb, kh)}:
+        i0 = int(kj[(kb == b) & (kh == kvh)].min()) if causal else 0
+        for hh in range(g):
+            parts.append((b * n_q + kvh * g + hh) * L + np.arange(i0, L))
+    need = np.unique(np.concatenate(parts)).astype(np.int64)
+    say(f"  oracle statistics for {need.size} query rows")
+    o_rows, lse_rows, delta_rows = oracle.attention_bwd_rowstats(q, k, v, do, scale, causal,
+                                                                 rows=need)
+    n_all = B * n_q * L
+    o_full = np.zeros((n_all, d))
+    lse_full = np.full(n_all, np.nan)
+    delta_full = np.full(n_all, np.nan)
+    o_full[need], lse_full[need], delta_full[need] = o_rows, lse_rows, delta_rows
+    o_bits = inputs.bf16_bits(o_full.astype(np.float32)).reshape(q.shape)
+    lse_dev = np.where(np.isnan(lse_full), 0.0, lse_full).astype(np.float32).reshape(B, n_q, L)
     tq, tk, tv, tdo, to = (to_dev(x) for x in (q, k, v, do, o_bits))
-    tl = torch.from_numpy(lse_o.astype(np.float32).reshape(B, n_q, L)).cuda()
+    tl = torch.from_numpy(lse_dev).cuda()
     dq, dk, dv, dl = attn_prefill_backward(tq, tk, tv, to, tl, tdo, scale=scale, causal=causal)
     torch.cuda.synchronize()
     dq = from_dev_bf16(dq).reshape(-1, d)
     dk = from_dev_bf16(dk).reshape(-1, d)
     dv = from_dev_bf16(dv).reshape(-1, d)
     dl = dl.cpu().numpy().astype(np.float64).reshape(-1)
-    if q_rows is None:
-        q_rows = np.arange(B * n_q * L)
-    if k_rows is None:
-        k_rows = np.arange(B * n_kv * L)
-    rq, bq = oracle.attention_bwd_dq(q, k, v, do, scale, causal, lse, delta, q_rows, absd)
-    rk, rv, bk, bv = oracle.attention_bwd_dkdv(q, k, v, do, scale, causal, lse, delta, k_rows,
-                                               absd)
+    rq = oracle.attention_bwd_dq(q, k, v, do, scale, causal, lse_full, delta_full, q_rows)
+    rk, rv = oracle.attention_bwd_dkdv(q, k, v, do, scale, causal, lse_full, delta_full, k_rows)
+    # the bounds, group by group
+    qv, kv_, vv, dov = (inputs.bf16_to_f32(x).astype(np.float64) for x in (q, k, v, do))
+    ov = o_full.reshape(B, n_q, L, d)
+    bq = np.empty_like(rq)
+    bk = np.empty_like(rk)
+    bv = np.empty_like(rv)
+    for b, kvh in groups:
+        hs = slice(kvh * g, kvh * g + g)
+        grp = bounds.BwdGroup(qv[b, hs], kv_[b, kvh], vv[b, kvh], dov[b, hs], ov[b, hs],
+                              lse_full.reshape(B, n_q, L)[b, hs],
+                              delta_full.reshape(B, n_q, L)[b, hs], scale, causal)
+        sel = np.nonzero((q_rows // (n_q * L) == b) & ((q_rows // L) % n_q // g == kvh))[0]
+        if sel.size:
+            bq[sel] = grp.dq_bound((q_rows[sel] // L) % n_q - kvh * g, q_rows[sel] % L, rq[sel])
+        sel = np.nonzero((k_rows // (n_kv * L) == b) & ((k_rows // L) % n_kv == kvh))[0]
+        if sel.size:
+            bk[sel], bv[sel] = grp.dkdv_bound(k_rows[sel] % L, rk[sel], rv[sel])
     _check(name + " dQ", dq[q_rows], rq, bq)
     _check(name + " dK", dk[k_rows], rk, bk)
     _check(name + " dV", dv[k_rows], rv, bv)
-    # delta from the bf16 output: within (2^-8 + 2^-16) sum |dO O| of the exact one
-    d_bound = (2.0 ** -8 + 2.0 ** -16) * absd + 1e-6
-    _check(name + " delta", dl, delta, d_bound)
+    # delta from the bf16 output, on the rows fed the oracle's output
+    d_bound = bounds.bwd_delta_bound(dov.reshape(-1, d)[need], o_rows) + 1e-6
+    _check(name + " delta", dl[need], delta_rows, d_bound)
 
 
 SHAPES = [
@@ -103,19 +148,29 @@ def test_bwd_parity(B, L, n_q, n_kv, d, causal):
     _run_case(B, L, n_q, n_kv, d, causal, seed=200 + L + n_q + d)
 
 
-@pytest.mark.parametrize("index", [2, 3])
+@pytest.mark.parametrize("index", [2, 3, 4, 5])
 def test_bwd_workload_group_parity(index):
     # one key/value group of the workload at full length (groups are
-    # independent), sampled rows: 512 query rows and 256 key rows
+    # independent): 512 sampled query rows and 256 sampled key rows.  For the
+    # 128K-token GQA-6 layer the key rows come from the last 2048 positions,
+    # so that the oracle needs the statistics of 6 x 2048 query rows instead
+    # of the whole layer's; its dQ rows are anywhere (each needs only its own
+    # statistics), so the full-length key sums of dQ are checked there, and the
+    # full-length query sums of dK and dV at the 32K-token GQA-8 layer.
     cfg = config(index)
     g = cfg.n_q // cfg.n_kv
+    L = cfg.L
     rng = np.random.default_rng(cfg.seed + 9)
-    q_rows = np.sort(rng.choice(g * cfg.L, 512, replace=False))
-    k_rows = np.sort(rng.choice(cfg.L, 256, replace=False))
-    q_rows = np.union1d(q_rows, [0, cfg.L - 1, g * cfg.L - 1])
-    k_rows = np.union1d(k_rows, [0, 127, 128, cfg.L - 1])
-    _run_case(1, cfg.L, g, 1, cfg.d_h, cfg.causal, cfg.seed, q_rows, k_rows,
-              label=f"bwd config{index} one group (L={cfg.L}, g={g})")
+    q_rows = np.sort(rng.choice(g * L, 512, replace=False))
+    q_rows = np.union1d(q_rows, [0, L - 1, g * L - 1])
+    if index == 5:
+        k_rows = np.sort(rng.choice(np.arange(L - 2048, L), 256, replace=False))
+        k_rows = np.union1d(k_rows, [L - 2048, L - 1])
+    else:
+        k_rows = np.sort(rng.choice(L, 256, replace=False))
+        k_rows = np.union1d(k_rows, [0, 127, 128, L - 1])
+    _run_case(1, L, g, 1, cfg.d_h, cfg.causal, cfg.seed, q_rows, k_rows,
+              label=f"bwd config{index} one group (L={L}, g={g})")
 
 
 def test_bwd_pipeline_and_errors():

@@ -132,46 +132,3 @@ def test_bwd_selected_rows_match_full():
     assert np.array_equal(dvs, dv.reshape(-1, d)[krows])
     with pytest.raises(ValueError):
         oracle.attention_bwd_dq(q, k, v, do, 0.3, 1, lse, delta, np.array([280]))
-
-
-def test_bwd_rounding_bound_holds_in_simulation():
-    # emulate a kernel that recomputes P in fp32 from an fp32 LSE, takes D
-    # from O rounded to bf16, rounds P and dS to bf16 for the products and
-    # the gradients to bf16 once; every gradient element must lie within the
-    # oracle's bound of the exact value
-    B, L, n_q, n_kv, d, causal, scale = 1, 48, 4, 2, 32, 1, 0.2
-    g = n_q // n_kv
-    q, k, v, do = _case(B, L, n_q, n_kv, d, seed=12)
-    lse, delta, absd = oracle.attention_bwd_rowstats(q, k, v, do, scale, causal)
-    rows = np.arange(B * n_q * L)
-    krows = np.arange(B * n_kv * L)
-    dq, bq = oracle.attention_bwd_dq(q, k, v, do, scale, causal, lse, delta, rows, absd)
-    dk, dv, bk, bv = oracle.attention_bwd_dkdv(q, k, v, do, scale, causal, lse, delta, krows, absd)
-    o, _, _ = oracle.attention_rows(q, k, v, scale, causal)
-    rb = lambda x: inputs.bf16_to_f32(inputs.bf16_bits(np.asarray(x, dtype=np.float32))).astype(np.float64)
-    qv, kv_, vv, dov = (_vals(x)[0] for x in (q, k, v, do))
-    o_b = rb(o).reshape(n_q, L, d)
-    sc32 = np.float32(scale)
-    log2e = np.float32(1.4426950408889634)
-    sim_dq = np.zeros((n_q, L, d))
-    sim_dk = np.zeros((n_kv, L, d))
-    sim_dv = np.zeros((n_kv, L, d))
-    for h in range(n_q):
-        kh = h // g
-        s32 = (qv[h].astype(np.float32) @ kv_[kh].astype(np.float32).T)  # exact products, fp32 sums
-        l32 = np.float32(lse.reshape(n_q, L)[h]) * log2e
-        p32 = np.exp2(s32 * (sc32 * log2e) - l32[:, None]).astype(np.float32)
-        mask = np.tril(np.ones((L, L), bool)) if causal else np.ones((L, L), bool)
-        p32 = np.where(mask, p32, 0).astype(np.float32)
-        dp32 = (dov[h].astype(np.float32) @ vv[kh].astype(np.float32).T)
-        d32 = np.sum(dov[h].astype(np.float32) * o_b[h].astype(np.float32), axis=1)
-        ds32 = p32 * (dp32 - d32[:, None])
-        pb, dsb = rb(p32), rb(ds32)
-        sim_dv[kh] += pb.T @ dov[h]
-        sim_dk[kh] += float(sc32) * (dsb.T @ qv[h])
-        sim_dq[h] = float(sc32) * (dsb @ kv_[kh])
-    sim_dq, sim_dk, sim_dv = rb(sim_dq), rb(sim_dk), rb(sim_dv)
-    for name, sim, ref, bnd in (("dq", sim_dq, dq, bq), ("dk", sim_dk, dk, bk), ("dv", sim_dv, dv, bv)):
-        err = np.abs(sim.reshape(-1, d) - ref)
-        assert np.all(err <= bnd + 1e-12), (name, float(np.max(err - bnd)))
-        assert np.max(err / (bnd + 1e-30)) > 0.05, name   # and the bound is not vacuous

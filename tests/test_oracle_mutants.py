@@ -5,7 +5,6 @@ plausibly make; it is compiled on the CPU into a temporary library, and at
 least one of the pin checks below has to fail on it, while all of them pass on
 the real oracle.  This guards the pins themselves.
 """
-import math
 import os
 
 import numpy as np
@@ -31,7 +30,6 @@ MUTANTS = {
     "e4m3 subnormals as normals": ("x = ldexp((double)m, -9);", "x = ldexp(1.0 + m / 8.0, -6);"),
     "descale ignored": ("return widen_e4m3(((const uint8_t *)base)[idx]) * mul;",
                         "return widen_e4m3(((const uint8_t *)base)[idx]); (void)mul;"),
-    "bound without weights": ("weighted += w[j] * a;", "weighted += a / n_vis;"),
     "dS sign in dQ": ("p * (bwd_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j) - delta[row])",
                       "p * (delta[row] - bwd_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j))"),
     "delta not subtracted in dK": ("p * (bwd_dp(v, dout, L, n_q, n_kv, d_h, b, h, i, j) - delta[qrow_id])",
@@ -41,8 +39,8 @@ MUTANTS = {
     "dV from dS": ("ov[t] += p * widen_bf16(drow[t]);", "ov[t] += ds * widen_bf16(drow[t]);"),
     "dK from dO": ("ok[t] += sc * ds * widen_bf16(qrow[t]);",
                    "ok[t] += sc * ds * widen_bf16(drow[t]); (void)qrow;"),
-    "delta without O": ("acc += widen_bf16(dout[r * d_h + t]) * o[r * d_h + t];",
-                        "acc += widen_bf16(dout[r * d_h + t]);"),
+    "delta without O": ("acc += widen_bf16(dout[row * d_h + t]) * o[r * d_h + t];",
+                        "acc += widen_bf16(dout[row * d_h + t]);"),
     "kv head h mod n_kv": ("const int64_t kvh = h / g;", "const int64_t kvh = h % n_kv;"),
     "log2 in lse": ("*lse = m + log(total);", "*lse = m + log2(total);"),
     "K read transposed": ("dot += elem(kind, q, qrow + t, dq) * elem(kind, k, krow + t, dk);",
@@ -117,9 +115,8 @@ def _check_chunk_brute(lib):
 
 
 def _check_fp8(lib):
-    # the e4m3 decoder against torch, the fp8 path against the bf16 path on
-    # values both hold exactly (power-of-two descales), and the rounding
-    # bound against a direct simulation
+    # the e4m3 decoder against torch and the fp8 path against the bf16 path on
+    # values both hold exactly (power-of-two descales)
     torch = pytest.importorskip("torch")
     tab = oracle.e4m3_table(lib=lib)
     ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
@@ -128,29 +125,10 @@ def _check_fp8(lib):
     q, k, v, *_ = inputs.make_fp8_qkv(1, 6, 20, 2, 1, 8, 86)
     dq, dk, dv = 0.25, 0.5, 2.0
     to_b = lambda c, s_: inputs.bf16_bits((ref[c] * s_).astype(np.float32))
-    o8, l8, bnd, _ = oracle.attention_rows_chunk_fp8(q, k, v, 0.7, dq, dk, dv, True, 14, lib=lib)
+    o8, l8, _ = oracle.attention_rows_chunk_fp8(q, k, v, 0.7, dq, dk, dv, True, 14, lib=lib)
     ob, lb, _ = oracle.attention_rows_chunk(to_b(q, dq), to_b(k, dk), to_b(v, dv), 0.7, True,
                                             q_offset=14, lib=lib)
-    if not (np.max(np.abs(o8 - ob)) <= 1e-15 and np.max(np.abs(l8 - lb)) <= 1e-15):
-        return False
-    vv = ref[v][0, 0] * dv
-    qv, kv_ = ref[q][0] * dq, ref[k][0, 0] * dk
-    for h in range(2):
-        for i in range(6):
-            r = h * 6 + i
-            sc = kv_[:15 + i] @ qv[h, i] * float(np.float32(0.7)) / math.log(2)
-            p = np.exp2(sc - sc.max())
-            p_hat = ref[inputs.e4m3_bits(p.astype(np.float32))]
-            err = np.abs((p_hat @ vv[:15 + i]) / p.sum() - o8[r])
-            if np.any(err > bnd[r] * (1 + 1e-9) + 1e-12):
-                return False
-            # and it is the stated expression, not merely some valid bound
-            P = p / p.sum()
-            a = np.abs(vv[:15 + i])
-            want = 2.0 ** -4 * (P @ a) + 2.0 ** -10 * P.max() * a.sum(axis=0)
-            if np.max(np.abs(bnd[r] - want)) > 1e-12 * max(1.0, np.max(want)):
-                return False
-    return True
+    return bool(np.max(np.abs(o8 - ob)) <= 1e-15 and np.max(np.abs(l8 - lb)) <= 1e-15)
 
 
 def _check_bwd(lib):
