@@ -27,24 +27,26 @@
 //
 // CDNA4 mapping:
 //  * A workgroup covers 256 query columns: HWG heads of one group times
-//    BR = 256 / HWG rows.  By default it is 8 wave64s, two per SIMD, each
-//    owning one block of 32 columns: the two waves of a SIMD cover each
-//    other's latencies, and at d_h = 128 one wave's softmax work nearly fills
-//    the issue slots next to its own MFMAs, so a lone wave per SIMD stalls.
-//    Each K or V^T fragment read from LDS feeds one MFMA per block; the LDS
-//    (measured ~250 B/clk/CU for 16-byte reads) has room for that.  The
-//    kernel is also written for two blocks per wave (4 waves, one per SIMD,
-//    each fragment feeding two MFMAs), selectable at build time.
-//  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand, Q (held in
-//    VGPRs for the whole loop) the B operand.  In the 32x32 result lane l
-//    holds 16 keys of query column l % 32, so the row max and row sum are
-//    lane-local except for one exchange between lanes l and l ^ 32
-//    (v_permlane32_swap).
+//    BR = 256 / HWG rows, as 8 wave64s, two per SIMD, each owning a block of
+//    32 columns: the two waves of a SIMD cover each other's latencies, and at
+//    d_h = 128 one wave's softmax work nearly fills the issue slots next to
+//    its own MFMAs, so a lone wave per SIMD stalls.  Each K or V^T fragment
+//    read from LDS feeds one MFMA (32x32) or two (16x16); the LDS (measured
+//    ~250 B/clk/CU for 16-byte reads) has room for that.
+//  * Scores are computed transposed, S^T = K Q^T: K (from LDS) is the A
+//    operand, Q (held in VGPRs for the whole loop) the B operand.  Two MFMA
+//    shapes are built.  v_mfma_f32_32x32x16_bf16 (the default): lane l holds
+//    16 keys of query column l % 32 per 32-key half.  v_mfma_f32_16x16x32_bf16
+//    (ATTN_PREFILL_MFMA=16): lane l holds 8 keys of each of columns l % 16
+//    and 16 + l % 16.  Either way the row max and row sum are lane-local
+//    until the lanes of a column combine theirs (v_permlane32_swap, and
+//    v_permlane16_swap for 16x16), which only happens when the reference max
+//    moves and at the end.
 //  * The output is accumulated transposed, O^T += V^T P^T, with V^T as the A
 //    operand and P^T as the B operand.  The score result's register layout
-//    is used directly as the B operand (the 16 keys a lane holds are the
-//    contraction slots of two k-steps, in a permuted key order), so P never
+//    is used directly as the B operand (32x32: the 16 keys a lane holds are
+//    the contraction slots of two k-steps; 16x16: the 8 keys of each of its
+//    columns those of one k-step; both in a permuted key order), so P never
 //    leaves the registers.  V^T fragments in that key order come from the
 //    row-major V tile through the gfx950 LDS transpose read
 //    (ds_read_b64_tr_b16: in each group of 16 lanes, lane 4r+q supplies four
@@ -73,6 +75,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <mutex>
 
 #include "attn_prefill.h"
@@ -80,13 +83,8 @@
 
 namespace {
 
-#ifndef ATTN_BLOCKS_PER_WAVE
-#define ATTN_BLOCKS_PER_WAVE 1
-#endif
-// 32-column blocks per wave: 2 (4 waves, one per SIMD) or 1 (8 waves, two
-// per SIMD); a workgroup always covers kCols query columns
-constexpr int kBlocksPerWave = ATTN_BLOCKS_PER_WAVE;
 constexpr int kCols = 256;            // query columns (head, row) per workgroup
+constexpr int kWaves = kCols / 32;    // wave64s per workgroup, 32 query columns each
 constexpr int kBC = 64;               // keys per K/V tile
 constexpr float kSlack = 8.0f;        // rescale only past 2^8 growth
 
@@ -96,28 +94,80 @@ constexpr float kSlack = 8.0f;        // rescale only past 2^8 growth
 // zero for contiguous reads).  K: the 16 lanes of a 16-byte read take 16
 // consecutive rows at one chunk, so the chunk is XORed with the row's low
 // bits to land on 16 distinct 16-byte slots of a 256-byte bank window.  V:
-// the 32 lanes of a transpose read take 4 rows x 2 chunk pairs; XORing the
-// chunk with 4 (row & 3) (d_h = 128) puts the 8 32-byte pieces on distinct
-// slots.  For d_h = 64 two rows share a 256-byte window, hence the shifts.
+// with the 32x32 shape the 32 lanes of a transpose read take 4 rows x 2 chunk
+// pairs, and XORing the chunk with 4 (row & 3) (d_h = 128) puts the 8 32-byte
+// pieces on distinct slots.  The 16x16 shape's transpose reads take 8
+// consecutive rows x 1 chunk pair, which the same swizzle spreads over 4
+// slots (rows r and r + 4 share one: two cycles per read); a swizzle that
+// separates all 8 would need a read offset per fragment instead of per pair
+// of fragments, and the registers for those are what the 16x16 pipeline
+// lacks.  For d_h = 64 two rows share a 256-byte window, hence the shifts.
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
-template <int D>
+template <int D, int MS>
 __device__ __forceinline__ int v_swz(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
-template <int D, int HWG, int NB>
-__global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
+// Per-lane score and accumulator registers of the two MFMA shapes.
+//   32x32x16: the lane holds one query column (l % 32) and, per 32-key half,
+//     16 of its scores, keys 4 (l / 32) + 8 (e / 4) + e % 4 for e = 0..15;
+//     O^T in D / 32 tiles of 32 x 32.
+//   16x16x32: the lane holds two query columns (l % 16 and 16 + l % 16) and,
+//     per half, 8 scores of each, keys 4 (l / 16) + 16 (e / 4) + e % 4 for
+//     e = 0..7 (two 16-key blocks, S^T block kb = e / 4 in register e % 4);
+//     O^T in D / 16 x 2 tiles of 16 x 16.
+// In both, score e of a column is the contraction slot e (of k-step e / 8
+// for 32x32) of the P^T operand the lane supplies, so P never moves.
+template <int D, int MS>
+struct Mfma;
+template <int D>
+struct Mfma<D, 32> {
+  struct Scores { f32x16 v; };
+  struct Acc { f32x16 t[D / 32]; };
+  static constexpr int kCol = 1;              // query columns per lane
+  static constexpr int kSpc = 16;             // scores per column per half
+  static constexpr int kQks = D / 16;         // k-steps of Q K^T
+  static constexpr int kKw = 16;              // contraction depth of a k-step
+  __device__ static constexpr int off(int e) { return 8 * (e >> 2) + (e & 3); }
+  __device__ static float get(const Scores& s, int, int e) { return s.v[e]; }
+  __device__ static void set(Scores& s, int, int e, float x) { s.v[e] = x; }
+  __device__ static float aget(const Acc& a, int, int i) { return a.t[i >> 4][i & 15]; }
+  __device__ static void aset(Acc& a, int, int i, float x) { a.t[i >> 4][i & 15] = x; }
+};
+template <int D>
+struct Mfma<D, 16> {
+  struct Scores { f32x4 v[4]; };               // [kb * 2 + cb]
+  struct Acc { f32x4 t[D / 16][2]; };          // [db][cb]
+  static constexpr int kCol = 2;
+  static constexpr int kSpc = 8;
+  static constexpr int kQks = D / 32;
+  static constexpr int kKw = 32;
+  __device__ static constexpr int off(int e) { return 16 * (e >> 2) + (e & 3); }
+  __device__ static float get(const Scores& s, int c, int e) { return s.v[(e >> 2) * 2 + c][e & 3]; }
+  __device__ static void set(Scores& s, int c, int e, float x) { s.v[(e >> 2) * 2 + c][e & 3] = x; }
+  __device__ static float aget(const Acc& a, int c, int i) { return a.t[i >> 2][c][i & 3]; }
+  __device__ static void aset(Acc& a, int c, int i, float x) { a.t[i >> 2][c][i & 3] = x; }
+};
+
+template <int D, int HWG, int MS>
+__global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ out,
     float* __restrict__ lse, int Lq, int Lk, int q_off, int n_q, int n_kv, int n_qblk,
     int items_per_qblk, int n_items, float scale, int causal) {
-  constexpr int NW = kCols / (32 * NB);        // waves per workgroup
+  using SH = Mfma<D, MS>;
+  using Scores = typename SH::Scores;
+  using Acc = typename SH::Acc;
+  constexpr int NW = kWaves;                   // waves per workgroup
   constexpr int BR = kCols / HWG;              // query rows per workgroup
-  constexpr int KSTEPS = D / 16;               // k-steps of Q K^T
-  constexpr int TBLK = D / 32;                 // 32-row blocks of O^T
+  constexpr int NF = D / 16;                   // K, V^T and Q fragments per wave and half
+  constexpr int NCOL = SH::kCol;               // query columns per lane
+  constexpr int SPC = SH::kSpc;                // scores per column and half
+  constexpr int QKS = SH::kQks;                // k-steps of Q K^T
+  constexpr int NACC = D / 2 / NCOL;           // accumulator values per column
   constexpr int ROWB = 2 * D;                  // bytes per K or V row
   constexpr int TILE = kBC * ROWB;             // bytes per K or V tile
   constexpr int LOADS = TILE / (NW * 1024);    // 1 KB loads per wave per tile
@@ -126,19 +176,22 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
   constexpr int VRING = 0;                     // V ring at [0, 4 TILE)
   constexpr int KRING = RING * TILE;           // K ring at [4 TILE, 8 TILE)
 
-  // output staging: one 32-row output tile per (wave, block); half of them
-  // in the last ring slot, the other half in an area after the rings
-  constexpr int OT = 32 * ROWB;                // bytes of one block's output tile
+  // output staging: one 32-row output tile per wave; two of them in the last
+  // slot of each ring, the other four in an area after the rings
+  constexpr int OT = 32 * ROWB;                // bytes of one wave's output tile
   constexpr int STAGE = 2 * RING * TILE;       // staging area offset
-  static_assert(4 * OT == 2 * TILE && NW * NB == 8, "half the output tiles fill one ring slot");
+  static_assert(4 * OT == 2 * TILE && NW == 8, "half the output tiles fill one ring slot");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGE + 4 * OT];
   LDS_AS unsigned char* const smem_l = (LDS_AS unsigned char*)smem;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int hi = lane >> 5;     // which half of the wave
-  const int col = lane & 31;    // query column inside a 32-column block
+  // the lane's column inside its block of MS columns and its key group
+  const int lcol = lane & (MS - 1);
+  const int lgrp = lane / MS;
+  // query row offset (inside the wave's 32) of the lane's column c
+  auto col_off = [&] __device__ (int c) __attribute__((always_inline)) { return 16 * c + lcol; };
 
   // ---- work items: (b, kv-head, head group, q-block), numbered heavy
   // q-blocks first with neighbouring numbers on different heads.  The grid
@@ -181,36 +234,38 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     e.vb = v + ((size_t)e.b * n_kv + e.kvh) * (size_t)Lk * D;
     return e;
   };
-  // the wave's NB 32-column blocks: columns 32 (wave + NW ib) of the
-  // workgroup, column c being head c / BR, row c % BR of the q-block
-  auto blk_head = [&] __device__ (const Geo& e, int ib) __attribute__((always_inline)) {
-    return e.kvh * g + e.hg * HWG + 32 * (wave + NW * ib) / BR;
+  // the wave's 32 columns: columns 32 wave .. 32 wave + 31 of the workgroup,
+  // column c being head c / BR, row c % BR of the q-block
+  auto blk_head = [&] __device__ (const Geo& e) __attribute__((always_inline)) {
+    return e.kvh * g + e.hg * HWG + 32 * wave / BR;
   };
-  auto blk_q0 = [&] __device__ (const Geo& e, int ib) __attribute__((always_inline)) {
-    return e.qb * BR + 32 * (wave + NW * ib) % BR;
+  auto blk_q0 = [&] __device__ (const Geo& e) __attribute__((always_inline)) {
+    return e.qb * BR + 32 * wave % BR;
   };
 
-  // ---- Q fragments (B operand of S^T = K Q^T): Q[row][16 kk + 8 hi + 0..7]
-  bf16x8 qf[NB][KSTEPS];
+  // ---- Q fragments (B operand of S^T = K Q^T), fragment f = c QKS + kk:
+  // Q[row of column c][kKw kk + 8 lgrp + 0..7] (kKw: 16 or 32 per k-step)
+  bf16x8 qf[NF];
   auto load_q = [&] __device__ (const Geo& e) __attribute__((always_inline)) {
+    const int q0 = blk_q0(e);
+    const unsigned short* qhead = q + ((size_t)e.b * n_q + blk_head(e)) * Lq64 * D;
 #pragma unroll
-    for (int ib = 0; ib < NB; ++ib) {
-      const int qi = blk_q0(e, ib) + col;
-      const unsigned short* qrow =
-          q + (((size_t)e.b * n_q + blk_head(e, ib)) * Lq64 + (size_t)qi) * D;
+    for (int c = 0; c < NCOL; ++c) {
+      const int qi = q0 + col_off(c);
+      const unsigned short* qrow = qhead + (size_t)qi * D;
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
+      for (int kk = 0; kk < QKS; ++kk) {
         u32x4 raw = {0u, 0u, 0u, 0u};
-        if (qi < Lq) raw = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hi * 8);
-        qf[ib][kk] = __builtin_bit_cast(bf16x8, raw);
+        if (qi < Lq) raw = *reinterpret_cast<const u32x4*>(qrow + kk * SH::kKw + lgrp * 8);
+        qf[c * QKS + kk] = __builtin_bit_cast(bf16x8, raw);
       }
     }
   };
 
-  // per-item state the pipeline reads: the wave's block heads and first
-  // rows, the tiles the workgroup streams and the tiles this wave computes,
-  // the K/V rows of this item and of the next one
-  int hb[NB], q0b[NB];
+  // per-item state the pipeline reads: the wave's head and first row, the
+  // tiles the workgroup streams and the tiles this wave computes, the K/V
+  // rows of this item and of the next one
+  int hb = 0, q0b = 0;
   int n_tiles = 0, wave_tiles = 0;
   const unsigned short* kbase = k;
   const unsigned short* vbase = v;
@@ -229,156 +284,248 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     const int row = byte / ROWB;
     const int pos = (byte % ROWB) >> 4;
     k_src[s] = row * ROWB + ((pos ^ k_swz<D>(row)) << 4);
-    v_src[s] = row * ROWB + ((pos ^ v_swz<D>(row)) << 4);
+    v_src[s] = row * ROWB + ((pos ^ v_swz<D, MS>(row)) << 4);
   }
   auto load_tile = [&] __device__ (const unsigned short* base, const int (&src)[LOADS], int tile,
                        int lds_off) __attribute__((always_inline)) {
     dma_tile(base, src, LOADS, ROWB, tile * kBC, Lk, kBC, smem + lds_off + wave * LOADS * 1024);
   };
 
-  // ---- per-lane LDS read offsets
-  // K rows col (+32 jb), the A operand of S^T = K Q^T, k-step kk
-  int k_rd[KSTEPS];
+  // ---- per-lane LDS read offsets (half 0 of ring slot 0; half jb adds 32 rows)
+  // K fragment f, the A operand of S^T = K Q^T.  32x32: key lcol, k-step f,
+  // chunk 2 f + lgrp.  16x16: f = kb QKS + kk, key 16 kb + lcol, chunk
+  // 4 kk + lgrp.
+  // (16x16: key block 1 sits 16 rows after block 0 under the same swizzle,
+  // so only the QKS k-steps need offsets of their own)
+  int k_rd[QKS];
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk)
-    k_rd[kk] = KRING + col * ROWB + (((2 * kk + hi) ^ k_swz<D>(col)) << 4);
-  // V^T through ds_read_b64_tr_b16: lane 16G + 4r + qq reads V[key][t .. t+3],
-  // key = 16 ks + 8 u + 4 (G / 2) + r, t = 32 tb + 16 (G % 2) + 4 qq, and
-  // receives V^T[32 tb + lane % 32][keys]
-  int v_rd[TBLK];
+  for (int kk = 0; kk < QKS; ++kk) {
+    const int chunk = MS == 32 ? 2 * kk + lgrp : 4 * kk + lgrp;
+    k_rd[kk] = KRING + lcol * ROWB + ((chunk ^ k_swz<D>(lcol)) << 4);
+  }
+  // V^T fragment f through ds_read_b64_tr_b16 (in each group of 16 lanes,
+  // lane 4r+qq supplies four consecutive 16-bit values of row r and lane i
+  // receives column i of the four rows), two reads per fragment.
+  //   32x32: f = 2 tb + h; lane 16G + 4r + qq reads V[key][t .. t+3] with
+  //     key = 16 (2 jb + h) + 8 u + 4 (G / 2) + r, t = 32 tb + 16 (G % 2) + 4 qq,
+  //     u = 0, 1 the two reads (8 rows apart), and receives V^T[32 tb + l % 32]
+  //     at the keys of its P^T slots.
+  //   16x16: f = db; lane 16G + 4r + qq reads V[key][t .. t+3] with
+  //     key = 32 jb + 16 u + 4 G + r, t = 16 db + 4 qq, u = 0, 1 (16 rows
+  //     apart), and receives V^T[16 db + l % 16] at keys 16 u + 4 G + 0..3.
+  // (32x32: the k-step h of fragment 2 tb + h moves the rows by 16, which
+  // keeps the swizzle, so only the D / 32 column blocks need offsets)
+  constexpr int NVRD = D / 32;
+  int v_rd[NVRD];
   {
     const int tr_r = (lane >> 2) & 3;
     const int tr_q = lane & 3;
-    const int tr_g = (lane >> 4) & 1;
+    const int tr_g = lane >> 4;
 #pragma unroll
-    for (int tb = 0; tb < TBLK; ++tb) {
-      const int t = 32 * tb + 16 * tr_g + 4 * tr_q;
-      const int key = 4 * hi + tr_r;  // plus 16 ks + 8 u, which keep the swizzle
-      v_rd[tb] = VRING + key * ROWB + (((t >> 3) ^ v_swz<D>(key)) << 4) + ((t >> 2) & 1) * 8;
+    for (int f = 0; f < NVRD; ++f) {
+      int key, t;
+      if constexpr (MS == 32) {
+        key = 4 * (tr_g >> 1) + tr_r;                  // plus 32 jb + 16 h + 8 u
+        t = 32 * f + 16 * (tr_g & 1) + 4 * tr_q;
+      } else {
+        key = 4 * tr_g + tr_r;                         // plus 32 jb + 16 u
+        t = 32 * f + 4 * tr_q;                         // plus 16 for the odd fragments
+      }
+      v_rd[f] = VRING + key * ROWB + (((t >> 3) ^ v_swz<D, MS>(key)) << 4) + ((t >> 2) & 1) * 8;
     }
   }
+  constexpr int V_U = (MS == 32 ? 8 : 16) * ROWB;    // bytes between the two reads
 
-  // ---- running state per block: reference max m (log2 domain), lane
+  // ---- running state per column: reference max m (log2 domain), lane
   // partial row sum l, accumulator O^T
-  f32x16 acc[NB][TBLK];
-  float m_run[NB], l_run[NB];
+  Acc acc;
+  float m_run[NCOL], l_run[NCOL];
   const float c2 = scale * kLog2e;
   const bool fast_scale = c2 > 0.0f;
 
   // K fragments of ring slot `slot`, keys 32 jb .. 32 jb + 31
-  auto load_kfrags = [&] __device__ (bf16x8 (&kf)[KSTEPS], int slot, int jb) __attribute__((always_inline)) {
+  // (k-steps [kk0, kk1) only, for both key blocks of the 16x16 shape)
+  auto load_kfrags = [&] __device__ (bf16x8 (&kf)[NF], int slot, int jb, int kk0 = 0,
+                                     int kk1 = SH::kQks) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-      kf[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(smem_l + k_rd[kk] + slot * TILE +
-                                                       jb * 32 * ROWB);
+    for (int f = 0; f < NF; ++f)
+      if (f % QKS >= kk0 && f % QKS < kk1)
+        kf[f] = *reinterpret_cast<const LDS_AS bf16x8*>(smem_l + k_rd[f % QKS] + slot * TILE +
+                                                        (jb * 32 + 16 * (f / QKS)) * ROWB);
   };
-  // V^T fragments of ring slot `slot`, k-steps 2 jb and 2 jb + 1
-  auto load_vfrags = [&] __device__ (bf16x8 (&vf)[TBLK][2], int slot, int jb) __attribute__((always_inline)) {
+  // V^T fragments of ring slot `slot`, keys 32 jb .. 32 jb + 31
+  auto load_vfrags = [&] __device__ (bf16x8 (&vf)[NF], int slot, int jb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int tb = 0; tb < TBLK; ++tb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const LDS_AS unsigned char* base =
-            smem_l + v_rd[tb] + slot * TILE + (2 * jb + h) * 16 * ROWB;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base));
-        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base + 8 * ROWB));
-        vf[tb][h] = __builtin_bit_cast(
-            bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                            __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]});
-      }
-  };
-
-  // S^T = K Q^T for the wave's blocks, k-steps [k0, k1); each K fragment
-  // feeds NB MFMAs.  k0 = 0 starts from zero.
-  auto qk_mfma = [&] __device__ (f32x16 (&S)[NB], const bf16x8 (&kf)[KSTEPS], int k0, int k1)
-      __attribute__((always_inline)) {
-    if (k0 == 0) {
-#pragma unroll
-      for (int ib = 0; ib < NB; ++ib)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[ib][r] = 0.0f;
+    for (int f = 0; f < NF; ++f) {
+      const LDS_AS unsigned char* base =
+          smem_l + v_rd[f >> 1] + (f & 1) * (MS == 32 ? 16 * ROWB : 32) + slot * TILE +
+          jb * 32 * ROWB;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base));
+      const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base + V_U));
+      vf[f] = __builtin_bit_cast(
+          bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                          __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]});
     }
-#pragma unroll
-    for (int kk = k0; kk < k1; ++kk)
-#pragma unroll
-      for (int ib = 0; ib < NB; ++ib)
-        S[ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[ib][kk], S[ib], 0, 0, 0);
   };
 
-  // O^T += V^T P^T for one block (the TBLK accumulators interleave, so no
-  // MFMA waits on the one just issued)
-  auto pv_mfma = [&] __device__ (const bf16x8 (&vf)[TBLK][2], const bf16x8 (&pk)[2], int ib) __attribute__((always_inline)) {
+  // S^T = K Q^T, k-steps [k0, k1); k0 = 0 starts from zero.  The 16x16
+  // shape runs four independent chains (two key blocks x two columns).
+  auto qk_mfma = [&] __device__ (Scores& S, const bf16x8 (&kf)[NF], int k0, int k1)
+      __attribute__((always_inline)) {
+    if constexpr (MS == 32) {
+      if (k0 == 0)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+        for (int r = 0; r < 16; ++r) S.v[r] = 0.0f;
 #pragma unroll
-      for (int tb = 0; tb < TBLK; ++tb)
-        acc[ib][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[tb][h], pk[h], acc[ib][tb], 0, 0, 0);
+      for (int kk = k0; kk < k1; ++kk)
+        S.v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], S.v, 0, 0, 0);
+    } else {
+      if (k0 == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S.v[i][r] = 0.0f;
+#pragma unroll
+      for (int kk = k0; kk < k1; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            S.v[kb * 2 + c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                kf[kb * QKS + kk], qf[c * QKS + kk], S.v[kb * 2 + c], 0, 0, 0);
+    }
   };
 
-  // row max of one block's 32 scores per lane pair (branch-free)
-  auto row_max = [&] __device__ (const f32x16& s) __attribute__((always_inline)) {
-    float mx = fmaxf(s[0], s[1]);
+  // O^T += V^T P^T (consecutive MFMAs write different accumulators).  pk:
+  // 32x32: the two 16-key k-steps of the one column; 16x16: the one 32-key
+  // k-step of each of the two columns.
+  auto pv_mfma = [&] __device__ (const bf16x8 (&vf)[NF], const bf16x8 (&pk)[2]) __attribute__((always_inline)) {
+    if constexpr (MS == 32) {
 #pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    return pair_max(mx);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int tb = 0; tb < D / 32; ++tb)
+          acc.t[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[2 * tb + h], pk[h], acc.t[tb],
+                                                              0, 0, 0);
+    } else {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          acc.t[db][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pk[c], acc.t[db][c],
+                                                                 0, 0, 0);
+    }
+  };
+
+  // the lane's own maximum of column c's scores (branch-free; the lanes of a
+  // column combine theirs only when the reference moves)
+  auto lane_max = [&] __device__ (const Scores& s, int c) __attribute__((always_inline)) {
+    float mx = fmaxf(SH::get(s, c, 0), SH::get(s, c, 1));
+#pragma unroll
+    for (int e = 2; e < SPC; ++e) mx = fmaxf(mx, SH::get(s, c, e));
+    return mx;
+  };
+  // maximum / sum over the lanes that hold one column
+  auto col_max = [&] __device__ (float x) __attribute__((always_inline)) {
+    if constexpr (MS == 16) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                      false, false);
+      x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    return pair_max(x);
+  };
+  auto col_sum = [&] __device__ (float x) __attribute__((always_inline)) {
+    if constexpr (MS == 16) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                      false, false);
+      x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return pair_sum(x);
   };
 
   // softmax, first part, for the scores of keys j0 .. j0+31 (may branch):
   // where the half straddles the diagonal (query q0 + i sees keys up to
-  // q_off + q0 + i) or the end of the keys, or the
-  // scale is not positive, mask and pre-scale the scores and retake the row
-  // max; then move the reference max (rescaling l and acc) only when the
-  // tile max exceeds it by more than 2^8.  Returns the multiplier and -m.
-  auto prepare = [&] __device__ (f32x16& s, float mx, int ib, int j0, float& c_out,
-                                 float& mneg_out) __attribute__((always_inline)) {
-    const int q0 = q0b[ib];
-    const int qi = q0 + col;
-    const bool need_mask = (causal && j0 + 31 > q0 + q_off) || (j0 + 32 > Lk);
+  // q_off + q0 + i) or the end of the keys, or the scale is not positive,
+  // mask and pre-scale the scores.  Then move the reference max (rescaling l
+  // and acc) only when some lane's own maximum exceeds it by more than 2^8:
+  // no column's maximum can exceed it then, since a column's maximum is one
+  // of its lanes' maxima.  When it moves, every column takes the maximum of
+  // its lanes.  Returns the multiplier and -m per column.
+  auto prepare = [&] __device__ (Scores& s, int j0, float& c_out, float (&mneg)[NCOL])
+      __attribute__((always_inline)) {
+    // the lane maxima first (the common case needs them as they are), so
+    // their chain starts before the mask decision resolves
+    float mx[NCOL];
+#pragma unroll
+    for (int cc = 0; cc < NCOL; ++cc) mx[cc] = lane_max(s, cc);
+    const bool need_mask = (causal && j0 + 31 > q0b + q_off) || (j0 + 32 > Lk);
     float c = c2;
     if (need_mask || !fast_scale) {
-      // score r of this lane is key j0 + 4 hi + o_r, o_r = 8 (r / 4) + r % 4,
-      // visible to query qi (at key position qi + q_off) iff o_r <= lim.  A
-      // scale <= 0 is applied before masking, so that a masked score stays
-      // -inf; a positive one later, in the exponential.
-      const int lim = (causal ? min(qi + q_off, Lk - 1) : Lk - 1) - j0 - 4 * hi;
+      // score e of column c is key j0 + 4 lgrp + off(e), visible to query
+      // qi (at key position qi + q_off) iff off(e) <= lim.  A scale <= 0 is
+      // applied before masking, so that a masked score stays -inf; a
+      // positive one later, in the exponential.
       const float cm = fast_scale ? 1.0f : c2;
+      // (the lane id is re-derived here, opaque to the compiler, so that the
+      // per-lane limits are computed in this rarely taken branch instead of
+      // being kept, or spilled, across the tile loop)
+      int mlane;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(mlane));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = (r >> 2) * 8 + (r & 3) > lim ? -INFINITY : s[r] * cm;
+      for (int cc = 0; cc < NCOL; ++cc) {
+        const int qi = q0b + 16 * cc + (mlane & (MS - 1));
+        const int lim = (causal ? min(qi + q_off, Lk - 1) : Lk - 1) - j0 - 4 * (mlane / MS);
+#pragma unroll
+        for (int e = 0; e < SPC; ++e)
+          SH::set(s, cc, e, SH::off(e) > lim ? -INFINITY : SH::get(s, cc, e) * cm);
+        mx[cc] = lane_max(s, cc);
+      }
       c = fast_scale ? c2 : 1.0f;
-      mx = row_max(s);
     }
-    const float m_cand = mx * c;
-    if (__builtin_amdgcn_ballot_w64(m_cand > m_run[ib] + kSlack) != 0) {
-      const float m_new = fmaxf(m_run[ib], m_cand);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[ib] - m_new);
-      m_run[ib] = m_new;
-      l_run[ib] *= alpha;
+    float m_cand[NCOL];
+    bool grow = false;
 #pragma unroll
-      for (int tb = 0; tb < TBLK; ++tb)
+    for (int cc = 0; cc < NCOL; ++cc) {
+      m_cand[cc] = mx[cc] * c;
+      grow = grow || (m_cand[cc] > m_run[cc] + kSlack);
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[ib][tb][r] *= alpha;
+      for (int cc = 0; cc < NCOL; ++cc) {
+        const float m_new = fmaxf(m_run[cc], col_max(m_cand[cc]));
+        const float alpha = __builtin_amdgcn_exp2f(m_run[cc] - m_new);
+        m_run[cc] = m_new;
+        l_run[cc] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) SH::aset(acc, cc, i, SH::aget(acc, cc, i) * alpha);
+      }
     }
     c_out = c;
-    mneg_out = -m_run[ib];
+#pragma unroll
+    for (int cc = 0; cc < NCOL; ++cc) mneg[cc] = -m_run[cc];
   };
 
-  // softmax, second part (branch-free): p = 2^(c s - m), the fp32 row sum,
-  // and P^T rounded to bf16 as two B-operand fragments
-  auto expo = [&] __device__ (const f32x16& s, int ib, float c, float mneg, bf16x8 (&pk)[2])
-      __attribute__((always_inline)) {
-    float psum = 0.0f;
+  // softmax, second part (branch-free): p = 2^(c s - m), the fp32 row sums,
+  // and P^T rounded to bf16 as two B-operand fragments (32x32: the column's
+  // two k-steps; 16x16: one k-step per column)
+  auto expo = [&] __device__ (const Scores& s, float cm, const float (&mneg)[NCOL],
+                              bf16x8 (&pk)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      bf16x8 frag;
+    for (int cc = 0; cc < NCOL; ++cc) {
+      float psum = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[half * 8 + e], c, mneg));
-        psum += p;
-        frag[e] = (__bf16)p;
+      for (int half = 0; half < SPC / 8; ++half) {
+        bf16x8 frag;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(SH::get(s, cc, half * 8 + e), cm, mneg[cc]));
+          psum += p;
+          frag[e] = (__bf16)p;
+        }
+        pk[cc + half] = frag;
       }
-      pk[half] = frag;
+      l_run[cc] += psum;
     }
-    l_run[ib] += psum;
   };
 
   // Software pipeline over 32-key half-steps h = 2 t + jb.  Entering the
@@ -386,19 +533,19 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
   // fragments of half h+1 and the V^T fragments of half h.  The region first
   // puts a few QK^T MFMAs of h+1 on the pipe (they need nothing from the
   // softmax) and, in the first half of a tile, issues the tile loads; while
-  // those run it takes the row max and the first softmax part of h (mask and
-  // rescale decisions, rarely taken branches).  Then, branch-free: the rest
-  // of the scores of h+1 next to the exponentials of h, block by block, each
-  // followed by its P V, with the K fragments of h+2 and the V^T fragments
-  // of h+1 read from LDS meanwhile.  Past the wave's last half the region
-  // computes on stale LDS data whose results are never used.
+  // those run it takes the lane maxima and the first softmax part of h (mask
+  // and rescale decisions, rarely taken branches).  Then, branch-free: the
+  // rest of the scores of h+1 next to the exponentials of h, followed by its
+  // P V, with the K fragments of h+2 and the V^T fragments of h+1 read from
+  // LDS meanwhile.  Past the wave's last half the region computes on stale
+  // LDS data whose results are never used.
   struct Half {
-    f32x16 s[NB];
-    bf16x8 kf[KSTEPS];
-    bf16x8 vf[TBLK][2];
+    Scores s;
+    bf16x8 kf[NF];
+    bf16x8 vf[NF];
   };
   Half hA, hB;
-  constexpr int KA = NB == 2 ? 3 : 2;  // k-steps of h+1 issued ahead of the branches
+  constexpr int KA = 2;                 // k-steps of h+1 issued ahead of the branches
 
   // Tile t of an item sits in ring slot t % 4; the ring runs on across
   // items.  During tile t the workgroup requests stream position t + 3 into
@@ -424,23 +571,32 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     const int jb1 = jb ^ 1;
     const int slot2 = (ts + 1) & (RING - 1);
     const int jb2 = jb;
-    // keep the scheduler from pulling this region's row max up next to the
+    // keep the scheduler from pulling this region's softmax up next to the
     // previous region's last MFMAs (whose results it would then stall on)
     __builtin_amdgcn_sched_barrier(0);
     qk_mfma(nxt.s, cur.kf, 0, KA);
     if (jb == 0) issue_tile_loads(ts, t);
-    float cc[NB], mn[NB];
-    const int j0 = t * kBC + jb * 32;
-#pragma unroll
-    for (int ib = 0; ib < NB; ++ib) prepare(cur.s[ib], row_max(cur.s[ib]), ib, j0, cc[ib], mn[ib]);
-    load_kfrags(nxt.kf, slot2, jb2);
-    load_vfrags(nxt.vf, slot1, jb1);
-    qk_mfma(nxt.s, cur.kf, KA, KSTEPS);
-#pragma unroll
-    for (int ib = 0; ib < NB; ++ib) {
-      bf16x8 pk[2];
-      expo(cur.s[ib], ib, cc[ib], mn[ib], pk);
-      pv_mfma(cur.vf, pk, ib);
+    float cm, mn[NCOL];
+    prepare(cur.s, t * kBC + jb * 32, cm, mn);
+    if constexpr (MS == 32) {
+      load_kfrags(nxt.kf, slot2, jb2);
+      load_vfrags(nxt.vf, slot1, jb1);
+      qk_mfma(nxt.s, cur.kf, KA, QKS);
+    } else {
+      // (16x16 needs more registers for its per-column state: it holds only
+      // the first half of the next half-step's K fragments across a region,
+      // reads the second half here, once the first half is consumed, and the
+      // V^T fragments of h+1 once those of h are, so that one set of each is
+      // live instead of two)
+      load_kfrags(cur.kf, slot1, jb1, KA, QKS);
+      qk_mfma(nxt.s, cur.kf, KA, QKS);
+    }
+    bf16x8 pk[2];
+    expo(cur.s, cm, mn, pk);
+    pv_mfma(cur.vf, pk);
+    if constexpr (MS == 16) {
+      load_vfrags(nxt.vf, slot1, jb1);
+      load_kfrags(nxt.kf, slot2, jb2, 0, KA);
     }
   };
 
@@ -478,22 +634,16 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     nkbase = nx.kb;
     nvbase = nx.vb;
     n_tiles = cur.n_tiles;
-    int last_row = -1;
-#pragma unroll
-    for (int ib = 0; ib < NB; ++ib) {
-      hb[ib] = blk_head(cur, ib);
-      q0b[ib] = blk_q0(cur, ib);
-      if (q0b[ib] < Lq) last_row = max(last_row, min(q0b[ib] + 31, Lq - 1));
-    }
+    hb = blk_head(cur);
+    q0b = blk_q0(cur);
+    const int last_row = q0b < Lq ? min(q0b + 31, Lq - 1) : -1;
     wave_tiles = last_row < 0 ? 0 : (causal ? (last_row + q_off) / kBC + 1 : n_tiles);
 #pragma unroll
-    for (int ib = 0; ib < NB; ++ib) {
+    for (int cc = 0; cc < NCOL; ++cc) {
 #pragma unroll
-      for (int tb = 0; tb < TBLK; ++tb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[ib][tb][e] = 0.0f;
-      m_run[ib] = -INFINITY;
-      l_run[ib] = 0.0f;
+      for (int i = 0; i < NACC; ++i) SH::aset(acc, cc, i, 0.0f);
+      m_run[cc] = -INFINITY;
+      l_run[cc] = 0.0f;
     }
 
     // ---- prologue: the item's tiles 0..2 and its Q have landed (and the
@@ -503,7 +653,7 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     tile_barrier();
     if (wave_tiles > 0) {
       load_kfrags(hB.kf, 0, 0);
-      qk_mfma(hA.s, hB.kf, 0, KSTEPS);
+      qk_mfma(hA.s, hB.kf, 0, QKS);
       load_kfrags(hA.kf, 0, 1);
       load_vfrags(hA.vf, 0, 0);
     }
@@ -540,7 +690,7 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     }
 
     // ---- epilogue: O = acc / l in bf16, LSE = ln 2 * (m + log2 l).  Each
-    // block's 32 x d_h output tile goes through LDS (ring slot 3, or the
+    // wave's 32 x d_h output tile goes through LDS (ring slot 3, or the
     // staging area) so that the global stores are whole rows: 1 KB
     // per store instruction instead of 8-byte pieces of 32 different rows.
     // (The lane id is re-derived here, opaque to the compiler, so that the
@@ -548,44 +698,45 @@ __global__ __launch_bounds__(kCols / NB * 2) void attn_fwd_kernel(
     // spilled, across the tile loop.)
     int elane;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(elane));
-    const int ecol = elane & 31;
-    const int ehi = elane >> 5;
+    const int ecol = elane & (MS - 1);
+    const int egrp = elane / MS;
+    const int q0 = q0b;
+    LDS_AS unsigned char* ot =
+        smem_l + (wave < 2 ? VRING + 3 * TILE + wave * OT
+                           : wave < 4 ? KRING + 3 * TILE + (wave - 2) * OT : STAGE + (wave - 4) * OT);
 #pragma unroll
-    for (int ib = 0; ib < NB; ++ib) {
-      const float l_tot = pair_sum(l_run[ib]);
+    for (int cc = 0; cc < NCOL; ++cc) {
+      const float l_tot = col_sum(l_run[cc]);
       const float inv = 1.0f / l_tot;
-      const int q0 = q0b[ib];
-      if (hi == 0 && q0 + col < Lq && wave_tiles > 0)
-        lse[((size_t)cur.b * n_q + hb[ib]) * Lq64 + (size_t)(q0 + col)] =
-            (m_run[ib] + __log2f(l_tot)) * kLn2;
-      const int idx = wave * NB + ib;
-      LDS_AS unsigned char* ot =
-          smem_l + (idx < 2 ? VRING + 3 * TILE + idx * OT
-                            : idx < 4 ? KRING + 3 * TILE + (idx - 2) * OT : STAGE + (idx - 4) * OT);
-      // lane (col, hi) holds row col, columns 32 tb + 8 grp + 4 hi + 0..3
+      const int row = 16 * cc * (MS == 16) + ecol;       // output row inside the wave's 32
+      if (egrp == 0 && q0 + row < Lq && wave_tiles > 0)
+        lse[((size_t)cur.b * n_q + hb) * Lq64 + (size_t)(q0 + row)] =
+            (m_run[cc] + __log2f(l_tot)) * kLn2;
+      // 32x32: lane (ecol, egrp) holds row ecol, columns 32 tb + 8 grp +
+      // 4 egrp + 0..3 (accumulator values 16 tb + 4 grp + 0..3).
+      // 16x16: lane (ecol, egrp) holds row 16 c + ecol, columns 16 db +
+      // 4 egrp + 0..3 (values 4 db + 0..3).
 #pragma unroll
-      for (int tb = 0; tb < TBLK; ++tb)
+      for (int grp = 0; grp < NACC / 4; ++grp) {
+        bf16x4 o4;
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          bf16x4 o4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[ib][tb][grp * 4 + e] * inv);
-          const int chunk = tb * 4 + grp;                  // 16-byte chunk of the row
-          *reinterpret_cast<LDS_AS u32x2*>(ot + ecol * ROWB + ((chunk ^ k_swz<D>(ecol)) << 4) +
-                                           ehi * 8) = __builtin_bit_cast(u32x2, o4);
-        }
-      // read back whole rows: store st covers rows 1024 st / ROWB onwards
-      unsigned short* obase = out + (((size_t)cur.b * n_q + hb[ib]) * Lq64 + (size_t)q0) * D;
-#pragma unroll
-      for (int st = 0; st < OT / 1024; ++st) {
-        const int byte = st * 1024 + elane * 16;
-        const int row = byte / ROWB;
-        const int chunk = (byte % ROWB) >> 4;
-        const u32x4 v4 =
-            *reinterpret_cast<const LDS_AS u32x4*>(ot + row * ROWB + ((chunk ^ k_swz<D>(row)) << 4));
-        if (q0 + row < Lq && wave_tiles > 0)
-          *reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8) = v4;
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(SH::aget(acc, cc, grp * 4 + e) * inv);
+        const int col = MS == 32 ? 8 * grp + 4 * egrp : 16 * grp + 4 * egrp;
+        *reinterpret_cast<LDS_AS u32x2*>(ot + row * ROWB + (((col >> 3) ^ k_swz<D>(row)) << 4) +
+                                         ((col >> 2) & 1) * 8) = __builtin_bit_cast(u32x2, o4);
       }
+    }
+    // read back whole rows: store st covers rows 1024 st / ROWB onwards
+    unsigned short* obase = out + (((size_t)cur.b * n_q + hb) * Lq64 + (size_t)q0) * D;
+#pragma unroll
+    for (int st = 0; st < OT / 1024; ++st) {
+      const int byte = st * 1024 + elane * 16;
+      const int row = byte / ROWB;
+      const int chunk = (byte % ROWB) >> 4;
+      const u32x4 v4 =
+          *reinterpret_cast<const LDS_AS u32x4*>(ot + row * ROWB + ((chunk ^ k_swz<D>(row)) << 4));
+      if (q0 + row < Lq && wave_tiles > 0)
+        *reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8) = v4;
     }
     if (!has_next) break;
     cur = nx;
@@ -603,15 +754,24 @@ int pick_hwg(int g) {
   return 1;
 }
 
+// MFMA shape of the forward kernel: 32 (v_mfma_f32_32x32x16_bf16) unless
+// the environment variable ATTN_PREFILL_MFMA says 16 (or 32).  Both shapes
+// compute the same attention (they differ in the order of the fp32 sums);
+// the override exists for comparing them.
+int pick_mfma() {
+  const char* s = std::getenv("ATTN_PREFILL_MFMA");
+  if (s && s[0] == '1' && s[1] == '6' && s[2] == 0) return 16;
+  return 32;
+}
+
 // Sizes of one call; Lq = Lk and q_off = 0 for a whole-sequence prefill.
 struct Shape {
   int B, Lq, Lk, q_off, n_q, n_kv, d_h;
 };
 
-template <int D, int HWG>
+template <int D, int HWG, int MS>
 int launch(const void* q, const void* k, const void* v, void* out, float* lse, const Shape& sh,
            float scale, int causal, hipStream_t stream) {
-  constexpr int NB = kBlocksPerWave;
   constexpr int BR = kCols / HWG;
   const int n_qblk = (sh.Lq + BR - 1) / BR;
   const long long items_per_qblk = (long long)sh.B * sh.n_kv * ((sh.n_q / sh.n_kv) / HWG);
@@ -626,7 +786,7 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, c
       n_cu < 1)
     return ATTN_PREFILL_ERR_LAUNCH;
   const long long grid = n_items < n_cu ? n_items : n_cu;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, HWG, NB>), dim3((unsigned)grid), dim3(kCols / NB * 2), 0,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, HWG, MS>), dim3((unsigned)grid), dim3(kWaves * 64), 0,
                      stream,
                      static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
                      static_cast<const unsigned short*>(v), static_cast<unsigned short*>(out), lse,
@@ -635,17 +795,23 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, c
   return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
 }
 
-template <int D>
-int launch_d(const void* q, const void* k, const void* v, void* out, float* lse, const Shape& sh,
+template <int D, int MS>
+int launch_m(const void* q, const void* k, const void* v, void* out, float* lse, const Shape& sh,
              float scale, int causal, hipStream_t stream) {
   switch (pick_hwg(sh.n_q / sh.n_kv)) {
-    case 8: return launch<D, 8>(q, k, v, out, lse, sh, scale, causal, stream);
-    case 4: return launch<D, 4>(q, k, v, out, lse, sh, scale, causal, stream);
-    case 2: return launch<D, 2>(q, k, v, out, lse, sh, scale, causal, stream);
-    default: return launch<D, 1>(q, k, v, out, lse, sh, scale, causal, stream);
+    case 8: return launch<D, 8, MS>(q, k, v, out, lse, sh, scale, causal, stream);
+    case 4: return launch<D, 4, MS>(q, k, v, out, lse, sh, scale, causal, stream);
+    case 2: return launch<D, 2, MS>(q, k, v, out, lse, sh, scale, causal, stream);
+    default: return launch<D, 1, MS>(q, k, v, out, lse, sh, scale, causal, stream);
   }
 }
 
+template <int D>
+int launch_d(const void* q, const void* k, const void* v, void* out, float* lse, const Shape& sh,
+             float scale, int causal, hipStream_t stream) {
+  if (pick_mfma() == 32) return launch_m<D, 32>(q, k, v, out, lse, sh, scale, causal, stream);
+  return launch_m<D, 16>(q, k, v, out, lse, sh, scale, causal, stream);
+}
 // Argument checks shared by the entry points, then the launch.
 int check_and_launch(const void* q, const void* k, const void* v, void* out, float* lse,
                      const Shape& sh, float scale, int causal, hipStream_t stream) {
@@ -804,7 +970,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
     const int row = byte / ROWB;
     const int pos = (byte % ROWB) >> 4;
     k_src[s] = row * ROWB + ((pos ^ k_swz<D>(row)) << 4);
-    v_src[s] = row * ROWB + ((pos ^ v_swz<D>(row)) << 4);
+    v_src[s] = row * ROWB + ((pos ^ v_swz<D, 32>(row)) << 4);
   }
   int k_rd[KSTEPS];
 #pragma unroll
@@ -819,7 +985,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
     for (int tb = 0; tb < TBLK; ++tb) {
       const int t = 32 * tb + 16 * tr_g + 4 * tr_q;
       const int key = 4 * hi + tr_r;
-      v_rd[tb] = TILE + key * ROWB + (((t >> 3) ^ v_swz<D>(key)) << 4) + ((t >> 2) & 1) * 8;
+      v_rd[tb] = TILE + key * ROWB + (((t >> 3) ^ v_swz<D, 32>(key)) << 4) + ((t >> 2) & 1) * 8;
     }
   }
 
