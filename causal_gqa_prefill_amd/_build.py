@@ -24,14 +24,27 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile the HIP sources into LIB (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, "-o", tmp, *SRCS]
+# the matrix-core rate probe the benchmark reports as context (a library of
+# its own: nothing in the attention library uses it)
+CEILING_SRC = os.path.join(PKG, "csrc", "mfma_ceiling.hip")
+CEILING_LIB = os.path.join(PKG, "libmfma_ceiling.so")
+
+
+def _compile(srcs, lib, verbose, extra=()):
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile the HIP sources into LIB and the rate probe into CEILING_LIB
+    (always recompiles)."""
+    _compile(SRCS, LIB, verbose, extra)
+    _compile([CEILING_SRC], CEILING_LIB, verbose)
     return LIB
 
 
