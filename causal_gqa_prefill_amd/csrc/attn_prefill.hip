@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ out,
     float* __restrict__ lse, int Lq, int Lk, int q_off, int n_q, int n_kv, int n_qblk,
-    int items_per_qblk, int n_items, float scale, int causal) {
+    int items_per_qblk, int n_items, float scale, int causal, int hpx) {
   using SH = Mfma<D, MS>;
   using Scores = typename SH::Scores;
   using Acc = typename SH::Acc;
@@ -204,6 +204,14 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
   // sees items congruent to w mod 8: workgroups are dealt to the eight XCDs
   // in turn, so each XCD keeps working on the same (batch, kv-head) streams
   // when their count is a multiple of 8, and its L2 keeps serving their K/V.
+  //
+  // Short sequences (hpx > 0, chosen by the host when the numbers fit): a
+  // round instead gives each XCD hpx whole heads, every q-block of each
+  // (position p of round r: XCD x = p % 8, slot s = p / 8, head
+  // (8 r + x) hpx + s / n_qblk, q-block n_qblk - 1 - s % n_qblk), so the
+  // q-blocks of a head stream its K/V prefix side by side and the XCD's L2
+  // fetches each tile once.  The odd rounds' mirrored slots pair every
+  // q-block with the complementary one of another head, as above.
   const int g = n_q / n_kv;
   const int ngroups = g / HWG;
   const size_t Lq64 = (size_t)Lq;
@@ -221,8 +229,18 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
   };
   auto geo = [&] __device__ (int item) __attribute__((always_inline)) {
     Geo e;
-    e.qb = n_qblk - 1 - item / items_per_qblk;
-    int rest = item % items_per_qblk;
+    int rest;
+    if (hpx > 0) {
+      const int G = gridDim.x;
+      const int rr = item / G;
+      const int p = item - rr * G;
+      const int slot = p >> 3;
+      rest = ((rr << 3) + (p & 7)) * hpx + slot / n_qblk;
+      e.qb = n_qblk - 1 - slot % n_qblk;
+    } else {
+      e.qb = n_qblk - 1 - item / items_per_qblk;
+      rest = item % items_per_qblk;
+    }
     e.hg = rest % ngroups;
     rest /= ngroups;
     e.kvh = rest % n_kv;
@@ -786,12 +804,19 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, c
       n_cu < 1)
     return ATTN_PREFILL_ERR_LAUNCH;
   const long long grid = n_items < n_cu ? n_items : n_cu;
+  // whole heads per XCD and round when every round fills all slots of all
+  // eight XCDs with whole heads (then the rounds are full as well)
+  int hpx = 0;
+  if (grid % 8 == 0 && (grid / 8) % n_qblk == 0) {
+    const long long h = grid / 8 / n_qblk;
+    if (items_per_qblk % (8 * h) == 0) hpx = (int)h;
+  }
   hipLaunchKernelGGL((attn_fwd_kernel<D, HWG, MS>), dim3((unsigned)grid), dim3(kWaves * 64), 0,
                      stream,
                      static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
                      static_cast<const unsigned short*>(v), static_cast<unsigned short*>(out), lse,
                      sh.Lq, sh.Lk, sh.q_off, sh.n_q, sh.n_kv, n_qblk, (int)items_per_qblk,
-                     (int)n_items, scale, causal);
+                     (int)n_items, scale, causal, hpx);
   return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
 }
 

@@ -85,6 +85,29 @@ def test_many_items_per_workgroup(B, L, n_q, n_kv, d, causal):
                 name=f"many items B={B} L={L} n_q={n_q} n_kv={n_kv} d={d} causal={causal}")
 
 
+# Short sequences on a 256-CU grid take the head-grouped item order (every
+# q-block of a head on one XCD in the same round): 1, 2 and 4 heads per XCD
+# and round, several rounds.  One seeded row of every 32-row block of every
+# head is checked, so every work item is.
+GROUPED = [
+    # B, L, n_q, n_kv, d, causal
+    (8, 2048, 32, 8, 128, 1),    # GQA-4, 32 q-blocks of 64 rows: 1 head per XCD, 8 rounds
+    (16, 1024, 32, 8, 64, 1),    # 16 q-blocks: 2 heads per XCD, 8 rounds, d_h = 64
+    (8, 2048, 16, 16, 128, 1),   # MHA, 8 q-blocks of 256 rows: 4 heads per XCD, 8 rounds
+    (4, 2048, 16, 16, 128, 0),   # non-causal: 4 heads per XCD, 2 rounds
+]
+
+
+@pytest.mark.parametrize("B,L,n_q,n_kv,d,causal", GROUPED)
+def test_grouped_item_order(B, L, n_q, n_kv, d, causal):
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    rng = np.random.default_rng(4500 + B + L)
+    blocks = np.arange(0, B * n_q * L, 32, dtype=np.int64)
+    rows = blocks + rng.integers(0, 32, size=blocks.size)
+    _check_case(B, L, n_q, n_kv, d, causal, scale, seed=4500 + B + L, rows=rows,
+                name=f"grouped order B={B} L={L} n_q={n_q} n_kv={n_kv} d={d} causal={causal}")
+
+
 # ---------------------------------------------------------------------------
 # edge shapes: ragged L, every GQA ratio class, both head sizes, B > 1,
 # non-causal, scales other than 1/sqrt(d)
