@@ -75,6 +75,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstdlib>
 #include <mutex>
 
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ out,
     float* __restrict__ lse, int Lq, int Lk, int q_off, int n_q, int n_kv, int n_qblk,
-    int items_per_qblk, int n_items, float scale, int causal, int hpx) {
+    int items_per_qblk, int n_items, float scale, int causal, int sg) {
   using SH = Mfma<D, MS>;
   using Scores = typename SH::Scores;
   using Acc = typename SH::Acc;
@@ -205,19 +206,25 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
   // in turn, so each XCD keeps working on the same (batch, kv-head) streams
   // when their count is a multiple of 8, and its L2 keeps serving their K/V.
   //
-  // Short sequences (hpx > 0, chosen by the host when the numbers fit): a
-  // round instead gives each XCD hpx whole heads, every q-block of each
-  // (position p of round r: XCD x = p % 8, slot s = p / 8, head
-  // (8 r + x) hpx + s / n_qblk, q-block n_qblk - 1 - s % n_qblk), so the
-  // q-blocks of a head stream its K/V prefix side by side and the XCD's L2
-  // fetches each tile once.  The odd rounds' mirrored slots pair every
-  // q-block with the complementary one of another head, as above.
+  // Stream blocks (sg > 0, chosen by the host): the list is instead cut into
+  // super-groups of sg q-blocks (heaviest first); inside one, every (batch,
+  // kv-head) stream in turn lists its sg q-blocks (heavy first), each with
+  // its head groups.  Workgroup w = 8 s + x (XCD x, slot s) takes position
+  // (G / 8) x + s of each even round and G - 1 minus that of each odd one,
+  // so an XCD works on a run of G / 8 consecutive list entries: a stream's
+  // adjacent q-blocks, which read the same K/V prefix side by side, and the
+  // XCD's L2 fetches each tile once for all of them.  With sg = n_qblk
+  // (short sequences) a run holds whole heads.
   const int g = n_q / n_kv;
   const int ngroups = g / HWG;
   const size_t Lq64 = (size_t)Lq;
   auto item_at = [&] __device__ (int r) __attribute__((always_inline)) {
     const int G = gridDim.x;
     const int w = blockIdx.x;
+    if (sg > 0) {
+      const int pos = (G >> 3) * (w & 7) + (w >> 3);
+      return r * G + ((r & 1) ? G - 1 - pos : pos);
+    }
     if (!(r & 1)) return r * G + w;
     if ((G & 7) == 0) return r * G + (G - 8 - (w & ~7)) + (w & 7);
     return r * G + G - 1 - w;
@@ -229,20 +236,22 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
   };
   auto geo = [&] __device__ (int item) __attribute__((always_inline)) {
     Geo e;
-    int rest;
-    if (hpx > 0) {
-      const int G = gridDim.x;
-      const int rr = item / G;
-      const int p = item - rr * G;
-      const int slot = p >> 3;
-      rest = ((rr << 3) + (p & 7)) * hpx + slot / n_qblk;
-      e.qb = n_qblk - 1 - slot % n_qblk;
+    int rest;   // the (batch, kv-head) stream
+    if (sg > 0) {
+      const int span = sg * items_per_qblk;
+      const int k_sg = item / span;
+      const int in_sg = item - k_sg * span;
+      const int per = min(sg, n_qblk - k_sg * sg) * ngroups;
+      rest = in_sg / per;
+      const int in_st = in_sg - rest * per;
+      e.qb = n_qblk - 1 - (k_sg * sg + in_st / ngroups);
+      e.hg = in_st % ngroups;
     } else {
       e.qb = n_qblk - 1 - item / items_per_qblk;
       rest = item % items_per_qblk;
+      e.hg = rest % ngroups;
+      rest /= ngroups;
     }
-    e.hg = rest % ngroups;
-    rest /= ngroups;
     e.kvh = rest % n_kv;
     e.b = rest / n_kv;
     // query row i sits at key position q_off + i; K and V hold Lk rows
@@ -804,19 +813,33 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, c
       n_cu < 1)
     return ATTN_PREFILL_ERR_LAUNCH;
   const long long grid = n_items < n_cu ? n_items : n_cu;
-  // whole heads per XCD and round when every round fills all slots of all
-  // eight XCDs with whole heads (then the rounds are full as well)
-  int hpx = 0;
-  if (grid % 8 == 0 && (grid / 8) % n_qblk == 0) {
-    const long long h = grid / 8 / n_qblk;
-    if (items_per_qblk % (8 * h) == 0) hpx = (int)h;
+  // stream blocks.  Short sequences: whole heads per XCD and round when
+  // they fill every round exactly and the rounds pair up (every round then
+  // holds heavy and light q-blocks, and an unpaired last round would leave
+  // its heavy ones running alone).
+  int sg = 0;
+  if (grid % 8 == 0) {
+    const long long slots = grid / 8;
+    if (slots % n_qblk == 0 && items_per_qblk % (8 * (slots / n_qblk)) == 0 &&
+        (n_items / grid) % 2 == 0)
+      sg = n_qblk;
+    // long sequences: runs of one or two streams per XCD; the super-groups
+    // do not line up with the rounds, so only when there are many rounds and
+    // many super-groups (each spanning a small share of the causal weights)
+    // does the zigzag still even the work out (within 0.1% over a sweep of
+    // shapes)
+    else if (n_items >= 16 * grid) {
+      const long long ng = (sh.n_q / sh.n_kv) / HWG;
+      const long long run = std::min<long long>(n_qblk, std::max<long long>(1, slots / ng));
+      if (n_qblk >= 64 * run) sg = (int)run;
+    }
   }
   hipLaunchKernelGGL((attn_fwd_kernel<D, HWG, MS>), dim3((unsigned)grid), dim3(kWaves * 64), 0,
                      stream,
                      static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
                      static_cast<const unsigned short*>(v), static_cast<unsigned short*>(out), lse,
                      sh.Lq, sh.Lk, sh.q_off, sh.n_q, sh.n_kv, n_qblk, (int)items_per_qblk,
-                     (int)n_items, scale, causal, hpx);
+                     (int)n_items, scale, causal, sg);
   return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
 }
 

@@ -174,8 +174,9 @@ def test_bwd_workload_group_parity(index):
 
 
 def test_bwd_pipeline_and_errors():
-    # forward then backward on the GPU: gradients close to the isolated run;
-    # deterministic; errors raise
+    # forward then backward on the GPU: every gradient element within the
+    # rounding bound of the oracle's backward at the forward's own O and LSE
+    # (and within 2% of the largest exact gradient); deterministic; errors raise
     import torch
     from causal_gqa_prefill_amd import AttnPrefillError, attn_prefill, attn_prefill_backward
     say("case bwd pipeline")
@@ -190,12 +191,43 @@ def test_bwd_pipeline_and_errors():
     for a, b_ in zip(g1, g2):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                            b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_)
-    ref = oracle.attention_bwd(q, k, v, do, float(np.float32(d ** -0.5)), 1)
+    scale = float(np.float32(d ** -0.5))
+    ref = oracle.attention_bwd(q, k, v, do, scale, 1)
     for name, gpu, exact in (("dQ", g1[0], ref[0]), ("dK", g1[1], ref[1]), ("dV", g1[2], ref[2])):
         got = from_dev_bf16(gpu)
         rel = np.max(np.abs(got - exact)) / np.max(np.abs(exact))
         say(f"  pipeline {name}: max|d| / max|ref| = {rel:.3e}")
         assert rel <= 2e-2
+    # element by element: the oracle's gradients at the forward's own output
+    # and LSE (P from that LSE, delta = dO . O from that bf16 output) are what
+    # the backward kernels compute up to their rounding, so the per-element
+    # bound applies to the whole forward -> backward chain
+    o_fwd = from_dev_bf16(out).reshape(B, n_q, L, d)
+    lse_fwd = lse.cpu().numpy().astype(np.float64).reshape(B, n_q, L)
+    dov = inputs.bf16_to_f32(do).astype(np.float64)
+    delta_fwd = np.sum(dov * o_fwd, axis=-1)
+    rows_q = np.arange(B * n_q * L, dtype=np.int64)
+    rows_k = np.arange(B * n_kv * L, dtype=np.int64)
+    rq = oracle.attention_bwd_dq(q, k, v, do, scale, 1, lse_fwd.reshape(-1), delta_fwd.reshape(-1),
+                                 rows_q)
+    rk, rv = oracle.attention_bwd_dkdv(q, k, v, do, scale, 1, lse_fwd.reshape(-1),
+                                       delta_fwd.reshape(-1), rows_k)
+    qv, kv_, vv = (inputs.bf16_to_f32(x).astype(np.float64) for x in (q, k, v))
+    g = n_q // n_kv
+    bq = np.empty_like(rq)
+    bk = np.empty_like(rk)
+    bv = np.empty_like(rv)
+    for kvh in range(n_kv):
+        hs = slice(kvh * g, kvh * g + g)
+        grp = bounds.BwdGroup(qv[0, hs], kv_[0, kvh], vv[0, kvh], dov[0, hs], o_fwd[0, hs],
+                              lse_fwd[0, hs], delta_fwd[0, hs], scale, 1)
+        sel = np.arange(kvh * g * L, (kvh + 1) * g * L)
+        bq[sel] = grp.dq_bound(sel // L - kvh * g, sel % L, rq[sel])
+        sel = np.arange(kvh * L, (kvh + 1) * L)
+        bk[sel], bv[sel] = grp.dkdv_bound(sel % L, rk[sel], rv[sel])
+    _check("pipeline dQ", from_dev_bf16(g1[0]).reshape(-1, d), rq, bq)
+    _check("pipeline dK", from_dev_bf16(g1[1]).reshape(-1, d), rk, bk)
+    _check("pipeline dV", from_dev_bf16(g1[2]).reshape(-1, d), rv, bv)
     with pytest.raises(AttnPrefillError):
         attn_prefill_backward(tq, tk, tv, out, lse, tdo, scale=float("nan"))
     with pytest.raises(ValueError):

@@ -95,6 +95,8 @@ SHAPES = [
     (1, 2048, 8192, 6144, 16, 2, 1),    # a long chunk at an offset
     (160, 260, 260, 0, 8, 1, 1),        # 1440 work items: several per persistent workgroup
     (300, 40, 90, 50, 2, 2, 1),         # 600 chunk items of one or two tiles (MHA)
+    (4, 2048, 2048, 0, 16, 16, 1),      # whole heads per XCD and round: 4 heads, 2 rounds
+    (8, 1024, 1024, 0, 32, 8, 1),       # whole heads per XCD and round: 2 heads, 4 rounds
 ]
 
 

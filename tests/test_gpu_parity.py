@@ -85,16 +85,19 @@ def test_many_items_per_workgroup(B, L, n_q, n_kv, d, causal):
                 name=f"many items B={B} L={L} n_q={n_q} n_kv={n_kv} d={d} causal={causal}")
 
 
-# Short sequences on a 256-CU grid take the head-grouped item order (every
-# q-block of a head on one XCD in the same round): 1, 2 and 4 heads per XCD
-# and round, several rounds.  One seeded row of every 32-row block of every
-# head is checked, so every work item is.
+# Stream blocks (on a 256-CU grid): short sequences put every q-block of a
+# head on one XCD in the same round (1, 2 and 4 heads per XCD and round,
+# several rounds); very long ones give each XCD runs of adjacent q-blocks of
+# one or two (batch, kv-head) streams, cut into super-groups of 10 q-blocks
+# for g = 6 (the last one partial here).  One seeded row of every 32-row
+# block of every head is checked, so every work item is.
 GROUPED = [
     # B, L, n_q, n_kv, d, causal
     (8, 2048, 32, 8, 128, 1),    # GQA-4, 32 q-blocks of 64 rows: 1 head per XCD, 8 rounds
     (16, 1024, 32, 8, 64, 1),    # 16 q-blocks: 2 heads per XCD, 8 rounds, d_h = 64
     (8, 2048, 16, 16, 128, 1),   # MHA, 8 q-blocks of 256 rows: 4 heads per XCD, 8 rounds
     (4, 2048, 16, 16, 128, 0),   # non-causal: 4 heads per XCD, 2 rounds
+    (1, 82560, 24, 4, 128, 1),   # GQA-6, 645 q-blocks: 64 super-groups of 10 and one of 5
 ]
 
 
