@@ -61,7 +61,10 @@
 //    heavy-first list of work items, and the ring runs on across items: the
 //    next item's first tiles are requested into the slots the current
 //    item's last tiles free, and its Q is loaded while the current output is
-//    written, so an item no longer starts by waiting on HBM.
+//    written, so an item no longer starts by waiting on HBM.  Where the
+//    numbers fit, each XCD takes runs of adjacent q-blocks of one (batch,
+//    kv-head) stream (stream blocks, see item_at), so its L2 fetches a K/V
+//    tile once for all the workgroups that read it.
 //  * LDS rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads
 //    do not collide on banks (see k_swz / v_swz).
 //  * exp is exp2 with scale*log2(e) folded into one FMA; l and acc are only

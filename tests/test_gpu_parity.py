@@ -91,7 +91,7 @@ def test_many_items_per_workgroup(B, L, n_q, n_kv, d, causal):
 # one or two (batch, kv-head) streams, cut into super-groups of 10 q-blocks
 # for g = 6 (the last one partial here).  One seeded row of every 32-row
 # block of every head is checked, so every work item is.
-GROUPED = [
+STREAM_BLOCKS = [
     # B, L, n_q, n_kv, d, causal
     (8, 2048, 32, 8, 128, 1),    # GQA-4, 32 q-blocks of 64 rows: 1 head per XCD, 8 rounds
     (16, 1024, 32, 8, 64, 1),    # 16 q-blocks: 2 heads per XCD, 8 rounds, d_h = 64
@@ -101,14 +101,14 @@ GROUPED = [
 ]
 
 
-@pytest.mark.parametrize("B,L,n_q,n_kv,d,causal", GROUPED)
-def test_grouped_item_order(B, L, n_q, n_kv, d, causal):
+@pytest.mark.parametrize("B,L,n_q,n_kv,d,causal", STREAM_BLOCKS)
+def test_stream_block_item_order(B, L, n_q, n_kv, d, causal):
     scale = float(np.float32(1.0 / np.sqrt(d)))
     rng = np.random.default_rng(4500 + B + L)
     blocks = np.arange(0, B * n_q * L, 32, dtype=np.int64)
     rows = blocks + rng.integers(0, 32, size=blocks.size)
     _check_case(B, L, n_q, n_kv, d, causal, scale, seed=4500 + B + L, rows=rows,
-                name=f"grouped order B={B} L={L} n_q={n_q} n_kv={n_kv} d={d} causal={causal}")
+                name=f"stream blocks B={B} L={L} n_q={n_q} n_kv={n_kv} d={d} causal={causal}")
 
 
 # ---------------------------------------------------------------------------
