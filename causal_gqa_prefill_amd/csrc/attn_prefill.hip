@@ -101,17 +101,19 @@ constexpr float kSlack = 8.0f;        // rescale only past 2^8 growth
 // with the 32x32 shape the 32 lanes of a transpose read take 4 rows x 2 chunk
 // pairs, and XORing the chunk with 4 (row & 3) (d_h = 128) puts the 8 32-byte
 // pieces on distinct slots.  The 16x16 shape's transpose reads take 8
-// consecutive rows x 1 chunk pair, which the same swizzle spreads over 4
-// slots (rows r and r + 4 share one: two cycles per read); a swizzle that
-// separates all 8 would need a read offset per fragment instead of per pair
-// of fragments, and the registers for those are what the 16x16 pipeline
-// lacks.  For d_h = 64 two rows share a 256-byte window, hence the shifts.
+// consecutive rows x 1 chunk pair: XORing the chunk with 2 (row & 7) puts
+// them on 8 distinct slots (and keeps each 32-byte pair together).  That
+// swizzle moves the odd fragments' pair by +-32 bytes depending on the row,
+// so their read offset is the even fragment's XOR 32, formed at each read
+// (the pipeline has no registers for four more offsets).  For d_h = 64 two
+// rows share a 256-byte window, hence the shifts.
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
 template <int D, int MS>
 __device__ __forceinline__ int v_swz(int row) {
+  if (MS == 16) return D == 128 ? ((row & 7) << 1) : (((row >> 1) & 3) << 1);
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
@@ -359,7 +361,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
         t = 32 * f + 16 * (tr_g & 1) + 4 * tr_q;
       } else {
         key = 4 * tr_g + tr_r;                         // plus 32 jb + 16 u
-        t = 32 * f + 4 * tr_q;                         // plus 16 for the odd fragments
+        t = 32 * f + 4 * tr_q;                         // odd fragments: offset ^ 32
       }
       v_rd[f] = VRING + key * ROWB + (((t >> 3) ^ v_swz<D, MS>(key)) << 4) + ((t >> 2) & 1) * 8;
     }
@@ -383,12 +385,20 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
         kf[f] = *reinterpret_cast<const LDS_AS bf16x8*>(smem_l + k_rd[f % QKS] + slot * TILE +
                                                         (jb * 32 + 16 * (f / QKS)) * ROWB);
   };
+  // a ^ 32, computed where it is used (an opaque instruction the compiler
+  // cannot hoist out of the tile loop into registers of its own)
+  auto xor32 = [] __device__ (int a) __attribute__((always_inline)) {
+    int r;
+    asm volatile("v_xor_b32 %0, 32, %1" : "=v"(r) : "v"(a));
+    return r;
+  };
   // V^T fragments of ring slot `slot`, keys 32 jb .. 32 jb + 31
   auto load_vfrags = [&] __device__ (bf16x8 (&vf)[NF], int slot, int jb) __attribute__((always_inline)) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const LDS_AS unsigned char* base =
-          smem_l + v_rd[f >> 1] + (f & 1) * (MS == 32 ? 16 * ROWB : 32) + slot * TILE +
+          smem_l + (MS == 32 ? v_rd[f >> 1] + (f & 1) * 16 * ROWB
+                             : ((f & 1) ? xor32(v_rd[f >> 1]) : v_rd[f >> 1])) + slot * TILE +
           jb * 32 * ROWB;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base));
       const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base + V_U));
