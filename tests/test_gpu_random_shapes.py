@@ -1,12 +1,15 @@
-"""Seeded random shapes, forward pass through the C ABI against the oracle.
+"""Seeded random shapes through the C ABI against the oracle: the bf16
+forward (whole sequences and chunks), the FP8 forward and the backward.
 
 The hand-picked shapes of test_gpu_parity.py cover the edges one by one;
 this sweep draws batch, sequence length, head counts, group size, head size
 and mask at random (seeded) so that combinations nobody thought of are
 checked too, among them shapes whose persistent schedule takes stream
 blocks (whole heads per XCD and round) and shapes with partial last rounds.
-One seeded row of every 32-row block of every head is compared, so every
-work item of the launch is.  The benchmark spec's tolerances apply."""
+For the bf16 forward one seeded row of every 32-row block of every head is
+compared, so every work item of the launch is, within the forward's stated
+tolerances; the FP8 and backward cases compare every element within the
+rounding bounds of tests/bounds.py."""
 import numpy as np
 import pytest
 
@@ -134,3 +137,60 @@ def test_random_chunk(B, Lq, Lk, q_off, n_q, n_kv, d, causal):
     ref_o, ref_l, _ = oracle.attention_rows_chunk(qb, kb, vb, scale, causal, q_offset=q_off,
                                                   rows=rows)
     compare(label, o[rows], l[rows], ref_o, ref_l)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (e4m3, d_h = 128) and the backward pass on random shapes, each checked
+# element by element against the oracle within the rounding bounds of
+# tests/bounds.py (the helpers of test_gpu_fp8.py and test_gpu_bwd.py)
+# ---------------------------------------------------------------------------
+def _fp8_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        B, _, n_q, n_kv, _, causal = _draw(rng)
+        Lk = int(rng.choice([1, 65, 300, 1000, 2048]))
+        Lq = int(rng.integers(1, Lk + 1)) if causal else int(rng.choice([1, 31, 200]))
+        q_off = int(rng.integers(0, Lk - Lq + 1)) if causal else 0
+        if B * n_q * Lq * Lk > 1.5e8:
+            continue
+        out.append((B, Lq, Lk, q_off, n_q, n_kv, causal))
+    return out
+
+
+FP8_CASES = _fp8_cases(10, seed=9500)
+
+
+@pytest.mark.parametrize("B,Lq,Lk,q_off,n_q,n_kv,causal", FP8_CASES)
+def test_random_fp8(B, Lq, Lk, q_off, n_q, n_kv, causal):
+    from test_gpu_fp8 import _run_fp8, compare_fp8, fp8_reference
+    d = 128
+    label = f"random fp8 B={B} Lq={Lq} Lk={Lk} q_off={q_off} n_q={n_q} n_kv={n_kv} causal={causal}"
+    say(f"case {label}")
+    scale = float(np.float32(d ** -0.5))
+    q8, k8, v8, dq, dk, dv = inputs.make_fp8_qkv(B, Lq, Lk, n_q, n_kv, d,
+                                                 seed=9600 + B + Lq + 3 * Lk + q_off)
+    o, l = _run_fp8(q8, k8, v8, dq, dk, dv, scale, causal, q_off)
+    ref_o, ref_l, bound = fp8_reference(q8, k8, v8, scale, dq, dk, dv, causal, q_off)
+    compare_fp8(label, o.reshape(-1, d), l.reshape(-1), ref_o, ref_l, bound)
+
+
+def _bwd_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        B, L, n_q, n_kv, d, causal = _draw(rng)
+        if B * n_q * L * L > 4e7 or L > 2048:
+            continue
+        out.append((B, L, n_q, n_kv, d, causal))
+    return out
+
+
+BWD_CASES = _bwd_cases(8, seed=9700)
+
+
+@pytest.mark.parametrize("B,L,n_q,n_kv,d,causal", BWD_CASES)
+def test_random_backward(B, L, n_q, n_kv, d, causal):
+    from test_gpu_bwd import _run_case
+    _run_case(B, L, n_q, n_kv, d, causal, seed=9800 + B + L + n_q + d,
+              label=f"random bwd B={B} L={L} n_q={n_q} n_kv={n_kv} d={d} causal={causal}")
