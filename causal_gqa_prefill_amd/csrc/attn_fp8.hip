@@ -47,6 +47,11 @@
 #include "attn_prefill.h"
 #include "device_common.h"
 
+// the schedule of a persistent launch: static rounds, then a dynamic tail
+// through the returned counter pair (or none); defined with the bf16 kernels
+unsigned* attn_dyn_tail(long long n_items, long long grid, int causal, hipStream_t stream,
+                        long long* r_static);
+
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -81,7 +86,8 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
     const unsigned char* __restrict__ q, const unsigned char* __restrict__ k,
     const unsigned char* __restrict__ v, unsigned short* __restrict__ out,
     float* __restrict__ lse, int Lq, int Lk, int q_off, int n_q, int n_kv, int n_qblk,
-    int items_per_qblk, int n_items, float c2, float v_mul, int causal, int sg) {
+    int items_per_qblk, int n_items, float c2, float v_mul, int causal, int sg,
+    unsigned* __restrict__ dyn, int r_static) {
   constexpr int D = kF8D;
   constexpr int BR = kF8Cols / HWG;            // query rows per workgroup
   constexpr int KSTEPS = D / 64;               // 64-deep k-steps of Q K^T
@@ -392,15 +398,27 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
     load_tile(cur.kb, k_src, i, KRING + i * TILE);
     load_tile(cur.vb, v_src, i, VRING + i * TILE);
   }
+  // the word through which wave 0 passes a dynamic-tail item to the others
+  // (as in the bf16 kernel: the first bytes of its own output staging area)
+  LDS_AS int* const dyn_word = (LDS_AS int*)(smem_l + VRING + 3 * TILE);
+  const int n_dyn = n_items - r_static * (int)gridDim.x;
   for (;;) {
-    // ---- item setup
-    const int nxt_item = item_at(r + 1);
-    has_next = nxt_item < n_items;
-    const Geo nx = geo(has_next ? nxt_item : item);
+    // ---- item setup; the next item from the static schedule or, in the
+    // dynamic tail, from the call's counter (as in the bf16 kernel)
+    const bool dyn_next = dyn != nullptr && r + 1 >= r_static;
+    int nxt_item = n_items;
+    if (!dyn_next) {
+      nxt_item = item_at(r + 1);
+    } else if (wave == 0) {
+      if (lane == 0) {
+        const unsigned j = __hip_atomic_fetch_add(dyn, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_SYSTEM);
+        *dyn_word = j < (unsigned)n_dyn ? r_static * (int)gridDim.x + (int)j : n_items;
+      }
+      wait_lgkm0();
+    }
     kbase = cur.kb;
     vbase = cur.vb;
-    nkbase = nx.kb;
-    nvbase = nx.vb;
     n_tiles = cur.n_tiles;
     q0 = cur.q0;
     const int last_row = q0 < Lq ? min(q0 + 31, Lq - 1) : -1;
@@ -416,6 +434,15 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
     // previous item's stores are done); scores of unit 0, K fragments of unit 1
     wait_vmcnt<0>();
     tile_barrier();
+    if (dyn_next) {
+      nxt_item = __builtin_amdgcn_readfirstlane(*dyn_word);
+      wait_lgkm0();
+      tile_barrier();
+    }
+    has_next = nxt_item < n_items;
+    const Geo nx = geo(has_next ? nxt_item : item);
+    nkbase = nx.kb;
+    nvbase = nx.vb;
     if (wave_units > 0) {
       load_kfrags(kf, 0, 0);
       qk(SA, kf);
@@ -492,6 +519,13 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
     ++r;
   }
   wait_vmcnt<0>();   // no tile load may still be writing LDS when the wave ends
+  // the last workgroup out sets the call's counters back to zero
+  if (dyn != nullptr && wave == 0 && lane == 0 &&
+      __hip_atomic_fetch_add(dyn + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+          gridDim.x - 1) {
+    __hip_atomic_store(dyn, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(dyn + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
 }
 
 int f8_pick_hwg(int g) {
@@ -531,11 +565,15 @@ int f8_launch(const void* q, const void* k, const void* v, void* out, float* lse
       if (n_qblk >= 64 * run) sg = (int)run;
     }
   }
+  // the dynamic tail of the bf16 kernel's schedule
+  long long r_static = 0;
+  unsigned* dyn = attn_dyn_tail(n_items, grid, causal, stream, &r_static);
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<HWG>), dim3((unsigned)grid), dim3(64 * kF8Waves), 0,
                      stream, static_cast<const unsigned char*>(q),
                      static_cast<const unsigned char*>(k), static_cast<const unsigned char*>(v),
                      static_cast<unsigned short*>(out), lse, Lq, Lk, q_off, n_q, n_kv, n_qblk,
-                     (int)items_per_qblk, (int)n_items, c2, v_mul, causal, sg);
+                     (int)items_per_qblk, (int)n_items, c2, v_mul, causal, sg, dyn,
+                     (int)r_static);
   return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
 }
 

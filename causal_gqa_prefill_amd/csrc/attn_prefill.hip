@@ -64,7 +64,10 @@
 //    written, so an item no longer starts by waiting on HBM.  Where the
 //    numbers fit, each XCD takes runs of adjacent q-blocks of one (batch,
 //    kv-head) stream (stream blocks, see item_at), so its L2 fetches a K/V
-//    tile once for all the workgroups that read it.
+//    tile once for all the workgroups that read it.  A schedule of 16 or
+//    more rounds ends in a dynamic tail: the items of its last, lightest
+//    rounds go to whichever workgroup is free next (a counter per call), so
+//    the XCDs, which do not run equally fast, finish together.
 //  * LDS rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads
 //    do not collide on banks (see k_swz / v_swz).
 //  * exp is exp2 with scale*log2(e) folded into one FMA; l and acc are only
@@ -79,6 +82,7 @@
 #include <cmath>
 #include <cstdint>
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <mutex>
 
@@ -163,7 +167,8 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ out,
     float* __restrict__ lse, int Lq, int Lk, int q_off, int n_q, int n_kv, int n_qblk,
-    int items_per_qblk, int n_items, float scale, int causal, int sg) {
+    int items_per_qblk, int n_items, float scale, int causal, int sg, unsigned* __restrict__ dyn,
+    int r_static) {
   using SH = Mfma<D, MS>;
   using Scores = typename SH::Scores;
   using Acc = typename SH::Acc;
@@ -220,6 +225,11 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
   // adjacent q-blocks, which read the same K/V prefix side by side, and the
   // XCD's L2 fetches each tile once for all of them.  With sg = n_qblk
   // (short sequences) a run holds whole heads.
+  //
+  // Dynamic tail (dyn != nullptr, chosen by the host): only rounds
+  // 0 .. r_static - 1 follow item_at; the items from r_static G on go out in
+  // list order, one per draw from the call's counter, to the workgroups as
+  // they become free.
   const int g = n_q / n_kv;
   const int ngroups = g / HWG;
   const size_t Lq64 = (size_t)Lq;
@@ -664,15 +674,32 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
     load_tile(cur.kb, k_src, j, KRING + j * TILE);
     load_tile(cur.vb, v_src, j, VRING + j * TILE);
   }
+  // the word through which wave 0 passes a dynamic-tail item to the others:
+  // the first bytes of its own output staging area, which no other wave
+  // touches and no tile load writes between an item's epilogue and its
+  // successor's first tile step
+  LDS_AS int* const dyn_word = (LDS_AS int*)(smem_l + VRING + 3 * TILE);
+  const int n_dyn = n_items - r_static * (int)gridDim.x;
   for (;;) {
-    // ---- item setup
-    const int nxt_item = item_at(r + 1);
-    has_next = nxt_item < n_items;
-    const Geo nx = geo(has_next ? nxt_item : item);
+    // ---- item setup.  The next item: round r + 1 of the static schedule,
+    // or, in the dynamic tail, the next entry of the call's counter (taken
+    // by one lane while the prologue's loads land)
+    const bool dyn_next = dyn != nullptr && r + 1 >= r_static;
+    int nxt_item = n_items;
+    if (!dyn_next) {
+      nxt_item = item_at(r + 1);
+    } else if (wave == 0) {
+      if (lane == 0) {
+        // (system scope: performed past every XCD's L2, so that the
+        // workgroups of all XCDs count on one copy)
+        const unsigned j = __hip_atomic_fetch_add(dyn, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_SYSTEM);
+        *dyn_word = j < (unsigned)n_dyn ? r_static * (int)gridDim.x + (int)j : n_items;
+      }
+      wait_lgkm0();
+    }
     kbase = cur.kb;
     vbase = cur.vb;
-    nkbase = nx.kb;
-    nvbase = nx.vb;
     n_tiles = cur.n_tiles;
     hb = blk_head(cur);
     q0b = blk_q0(cur);
@@ -691,6 +718,17 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
     // fragments of half 1 and the V^T fragments of half 0 in registers
     wait_vmcnt<0>();
     tile_barrier();
+    if (dyn_next) {
+      // every wave reads the word before the barrier after which tile step
+      // 0 may overwrite it
+      nxt_item = __builtin_amdgcn_readfirstlane(*dyn_word);
+      wait_lgkm0();
+      tile_barrier();
+    }
+    has_next = nxt_item < n_items;
+    const Geo nx = geo(has_next ? nxt_item : item);
+    nkbase = nx.kb;
+    nvbase = nx.vb;
     if (wave_tiles > 0) {
       load_kfrags(hB.kf, 0, 0);
       qk_mfma(hA.s, hB.kf, 0, QKS);
@@ -784,6 +822,14 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
     ++r;
   }
   wait_vmcnt<0>();   // no tile load may still be writing LDS when the wave ends
+  // the last workgroup out (every other one has taken its last counter
+  // entry by then) sets the call's counters back to zero for the next call
+  if (dyn != nullptr && wave == 0 && lane == 0 &&
+      __hip_atomic_fetch_add(dyn + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+          gridDim.x - 1) {
+    __hip_atomic_store(dyn, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(dyn + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
 }
 
 // Heads per workgroup: the largest of 8, 4, 2, 1 that divides g.
@@ -803,6 +849,83 @@ int pick_mfma() {
   if (s && s[0] == '1' && s[1] == '6' && s[2] == 0) return 16;
   return 32;
 }
+
+// ---- the dynamic tail.  The eight XCDs of the chip do not run equally
+// fast (their shares of one launch finish up to 5% apart, the same XCDs
+// slow from launch to launch), which no static schedule can know.  The
+// forward kernels therefore run the first rounds of their heavy-first
+// schedule statically (each XCD on its own streams, for its L2) and hand out
+// the items of the last, lightest rounds through a counter that every
+// workgroup draws from when it is free, so that fast XCDs take more of them.
+//
+// Each call with a dynamic tail takes one pair of counters {next entry,
+// workgroups finished} from a per-GPU pool; the call's last workgroup sets
+// both back to zero, and a pair is handed out again only kDynSlots calls
+// later, so calls in flight at once on several streams never share one.
+// A call issued while its stream is being captured into a graph takes the
+// static schedule and no counter (a replayed graph would reuse one pair).
+constexpr int kDynSlots = 65536;
+constexpr int kDynMaxDevices = 64;
+static __device__ __align__(256) unsigned dyn_pool[2 * kDynSlots];
+std::mutex dyn_mu;
+unsigned* dyn_base[kDynMaxDevices] = {};
+std::atomic<unsigned> dyn_next_slot{0};
+
+// rounds of the static schedule before the dynamic tail: all of them when
+// there are fewer than kDynMinRounds (the workgroups of a short schedule
+// finish each round nearly together, so all of them would take a counter
+// entry at once, and those serialised atomics cost more than the balance
+// gains: 3-12% slower at 4 rounds, against 2.4-2.6% faster at 32 and 72);
+// otherwise the tail holds the last 30% of the rounds of a causal schedule
+// (about 9% of its work, the heavy-first rounds shrinking towards the end)
+// or the last 10% of a non-causal one
+constexpr long long kDynMinRounds = 16;
+long long static_rounds(long long n_items, long long grid, int causal) {
+  const long long R = (n_items + grid - 1) / grid;
+  if (R < kDynMinRounds) return R;
+  return R - (causal ? (3 * R + 9) / 10 : (R + 9) / 10);
+}
+
+// The counter pair of one call on the current GPU, or nullptr (static
+// schedule) while the stream is being captured or if the pool's address
+// cannot be had.
+unsigned* dyn_counters(hipStream_t stream) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+    return nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDynMaxDevices) return nullptr;
+  unsigned* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(dyn_mu);
+    if (dyn_base[dev] == nullptr) {
+      void* p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(dyn_pool)) != hipSuccess || p == nullptr)
+        return nullptr;
+      dyn_base[dev] = static_cast<unsigned*>(p);
+    }
+    base = dyn_base[dev];
+  }
+  return base + 2 * (dyn_next_slot.fetch_add(1, std::memory_order_relaxed) % kDynSlots);
+}
+
+}  // namespace
+
+// The schedule of a persistent launch of n_items items on grid workgroups:
+// *r_static rounds static, then the dynamic tail through the returned
+// counter pair, or (nullptr) every round static.  Shared with the FP8
+// kernel's launch.
+__attribute__((visibility("hidden"))) unsigned* attn_dyn_tail(long long n_items, long long grid,
+                                                              int causal, hipStream_t stream,
+                                                              long long* r_static) {
+  *r_static = static_rounds(n_items, grid, causal);
+  if (*r_static * grid >= n_items) return nullptr;
+  unsigned* dyn = dyn_counters(stream);
+  if (dyn == nullptr) *r_static = (n_items + grid - 1) / grid;
+  return dyn;
+}
+
+namespace {
 
 // Sizes of one call; Lq = Lk and q_off = 0 for a whole-sequence prefill.
 struct Shape {
@@ -847,12 +970,15 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, c
       if (n_qblk >= 64 * run) sg = (int)run;
     }
   }
+  // the dynamic tail, when the schedule has one and a counter pair is at hand
+  long long r_static = 0;
+  unsigned* dyn = attn_dyn_tail(n_items, grid, causal, stream, &r_static);
   hipLaunchKernelGGL((attn_fwd_kernel<D, HWG, MS>), dim3((unsigned)grid), dim3(kWaves * 64), 0,
                      stream,
                      static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
                      static_cast<const unsigned short*>(v), static_cast<unsigned short*>(out), lse,
                      sh.Lq, sh.Lk, sh.q_off, sh.n_q, sh.n_kv, n_qblk, (int)items_per_qblk,
-                     (int)n_items, scale, causal, sg);
+                     (int)n_items, scale, causal, sg, dyn, (int)r_static);
   return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
 }
 

@@ -39,13 +39,21 @@
  *
  * Ownership: the caller allocates and frees all five buffers, on the device
  * that is current when the call is made and that `stream` belongs to.  The
- * library allocates nothing, keeps no state between calls, never
- * synchronises, and may be called from several host threads at once.  out and
- * lse must not overlap each other or any input.
+ * library allocates nothing, never synchronises, and may be called from
+ * several host threads at once.  out and lse must not overlap each other or
+ * any input.
  *
- * Launch: the prefill kernels run a persistent grid of at most one
- * workgroup per CU of the current device (each walks several work items);
- * the result does not depend on the grid size.
+ * Launch: the prefill kernels (bf16 and FP8) run a persistent grid of at
+ * most one workgroup per CU of the current device (each walks several work
+ * items); the result does not depend on the grid size or on which
+ * workgroup computes an item.  A schedule of 16 or more rounds of work items
+ * hands out the items of its last rounds through a pair of counters that
+ * the call takes from a static per-device pool of 65536 pairs (512 KB of
+ * device memory held until the process ends): the call's last workgroup
+ * sets its pair back to zero, and a pair is handed out again only 65536
+ * calls later, so at most 65536 such calls may be in flight on one device
+ * at once.  A call made while its stream is being captured into a graph
+ * takes no pair (a static schedule, the same result).
  *
  * Errors: every argument is checked on the host before anything is enqueued.
  * A nonzero return means nothing was enqueued, except ATTN_PREFILL_ERR_LAUNCH,

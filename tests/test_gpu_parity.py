@@ -228,13 +228,16 @@ def test_non_default_stream():
 
 
 def test_concurrent_calls_on_two_streams_from_two_threads():
-    """The library keeps no state: two calls in flight at once (two host
-    threads, two streams, persistent grids competing for the same CUs) give
-    the same bits as the calls run one after the other."""
+    """Two calls in flight at once (two host threads, two streams, persistent
+    grids competing for the same CUs, each schedule ending in a dynamic tail
+    with a counter pair of its own) give the same bits as the calls run one
+    after the other."""
     import threading
     import torch
     from causal_gqa_prefill_amd import attn_prefill_into
-    shapes = [(4, 1024, 16, 4, 128, 1, 51), (2, 1500, 8, 8, 64, 1, 52)]
+    # 4096 work items each on 256 CUs: 16 rounds, the last 5 of them handed
+    # out through the counters
+    shapes = [(1, 16384, 64, 8, 128, 1, 51), (16, 2048, 32, 32, 64, 1, 52)]
     runs = []
     for (B, L, n_q, n_kv, d, causal, seed) in shapes:
         qb, kb, vb = inputs.make_qkv(B, L, n_q, n_kv, d, seed)
@@ -277,6 +280,92 @@ def test_concurrent_calls_on_two_streams_from_two_threads():
         same_l = torch.equal(outs[i][1].view(torch.int32), ref[i][1].view(torch.int32))
         say(f"  concurrent call {i}: output bits equal {same_o}, lse bits equal {same_l}")
         assert same_o and same_l
+
+
+# shapes whose schedules end in a dynamic tail on 256 CUs (at least 16
+# rounds; items, rounds): GQA-8 at 16K (4096, 16), MHA at 2K with 16
+# sequences (4096, 16), non-causal GQA-8 (4096, 16), a ragged GQA-6 sequence
+# with 64-wide heads (5778, 23: a partial last round)
+DYN_TAIL = [
+    (1, 16384, 64, 8, 128, 1),
+    (16, 2048, 32, 32, 64, 1),
+    (4, 4096, 64, 8, 64, 0),
+    (1, 41000, 36, 6, 64, 1),
+]
+
+
+@pytest.mark.parametrize("B,L,n_q,n_kv,d,causal", DYN_TAIL)
+def test_dynamic_tail_computes_every_item_once(B, L, n_q, n_kv, d, causal):
+    """Outputs poisoned with NaN, two calls in a row: every row of both is
+    written (an item the counter skipped would leave NaN; a counter pair not
+    set back to zero would make the second call skip its whole tail), both
+    calls give the same bits, and one seeded row of every 32-row block
+    matches the oracle."""
+    import torch
+    from causal_gqa_prefill_amd import attn_prefill_into
+    say(f"case dynamic tail B={B} L={L} n_q={n_q} n_kv={n_kv} d={d} causal={causal}")
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    qb, kb, vb = inputs.make_qkv(B, L, n_q, n_kv, d, seed=7000 + L + n_q)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    res = []
+    for _ in range(2):
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
+        attn_prefill_into(q, k, v, out, lse, scale=scale, causal=bool(causal))
+        torch.cuda.synchronize()
+        assert bool(torch.all(torch.isfinite(out.float()))), "an output row was not written"
+        assert bool(torch.all(torch.isfinite(lse))), "an lse entry was not written"
+        res.append((out, lse))
+    assert torch.equal(res[0][0].view(torch.int16), res[1][0].view(torch.int16))
+    assert torch.equal(res[0][1].view(torch.int32), res[1][1].view(torch.int32))
+    o = from_dev_bf16(res[0][0]).reshape(-1, d)
+    l = res[0][1].cpu().numpy().astype(np.float64).reshape(-1)
+    rng = np.random.default_rng(L)
+    blocks = np.arange(0, B * n_q * L, 32, dtype=np.int64)
+    rows = blocks + (rng.random(blocks.size) * np.minimum(32, B * n_q * L - blocks)).astype(np.int64)
+    ref_o, ref_l, _ = oracle.attention_rows(qb, kb, vb, scale, causal, rows=rows)
+    compare(f"dynamic tail L={L}", o[rows], l[rows], ref_o, ref_l)
+
+
+def test_graph_capture_takes_the_static_schedule():
+    """A call captured into a graph runs without a counter (the static
+    schedule); each replay, with eager calls (which do use counters) between
+    the replays, gives the eager call's bits."""
+    import torch
+    from causal_gqa_prefill_amd import attn_prefill_into
+    B, L, n_q, n_kv, d = 1, 16384, 64, 8, 128   # 16 rounds: a dynamic tail when eager
+    qb, kb, vb = inputs.make_qkv(B, L, n_q, n_kv, d, seed=7100)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    ref_o = torch.empty_like(q)
+    ref_l = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_prefill_into(q, k, v, ref_o, ref_l)
+    torch.cuda.synchronize()
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # one eager call on the capture stream first
+        attn_prefill_into(q, k, v, out, lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        attn_prefill_into(q, k, v, out, lse)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = (torch.equal(out.view(torch.int16), ref_o.view(torch.int16)) and
+                torch.equal(lse.view(torch.int32), ref_l.view(torch.int32)))
+        say(f"  replay {rep}: bits equal to the eager call {same}")
+        assert same
+        eo = torch.empty_like(q)
+        el = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        attn_prefill_into(q, k, v, eo, el)   # an eager call between replays
+        torch.cuda.synchronize()
+        assert torch.equal(eo.view(torch.int16), ref_o.view(torch.int16))
 
 
 def test_argument_errors_raise():
