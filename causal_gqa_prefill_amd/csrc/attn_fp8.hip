@@ -300,9 +300,10 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
         }
       c = 1.0f;
     } else {
+      // (a running max taking two scores per step: one v_max3 each)
       mx = fmaxf(S[0][0], S[1][0]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S[0][r], S[1][r]));
+      for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, S[0][r]), S[1][r]);
     }
     const float m_cand = pair_max(mx) * c;
     if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kF8Slack) != 0) {
@@ -316,7 +317,6 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
         for (int r = 0; r < 16; ++r) acc[tb][r] *= alpha;
     }
     const float mneg = -m_run;
-    float psum = 0.0f;
 #pragma unroll
     for (int bl = 0; bl < 2; ++bl)
 #pragma unroll
@@ -325,12 +325,15 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
         const float p1 = __builtin_amdgcn_exp2f(fmaf(S[bl][4 * w + 1], c, mneg));
         const float p2 = __builtin_amdgcn_exp2f(fmaf(S[bl][4 * w + 2], c, mneg));
         const float p3 = __builtin_amdgcn_exp2f(fmaf(S[bl][4 * w + 3], c, mneg));
-        psum += (p0 + p1) + (p2 + p3);
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        l_run += (p0 + p1) + (p2 + p3);
+        // the first conversion fills the low half of the word and keeps the
+        // high half, which the second one then writes: the word's previous
+        // bits are never used, so it starts as p0's own (a register that dies
+        // here) instead of a zeroed one
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __builtin_bit_cast(int, p0), false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
         pk[4 * bl + w] = word;
       }
-    l_run += psum;
   };
 
   auto pv = [&] __device__ (const i32x8 (&vf)[TBLK], const i32x8& pk)

@@ -555,26 +555,24 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
     for (int cc = 0; cc < NCOL; ++cc) mneg[cc] = -m_run[cc];
   };
 
-  // softmax, second part (branch-free): p = 2^(c s - m), the fp32 row sums,
-  // and P^T rounded to bf16 as two B-operand fragments (32x32: the column's
+  // softmax, second part (branch-free): p = 2^(c s - m) added to the lane's
+  // fp32 row sum, and P^T rounded to bf16 as two B-operand fragments (32x32: the column's
   // two k-steps; 16x16: one k-step per column)
   auto expo = [&] __device__ (const Scores& s, float cm, const float (&mneg)[NCOL],
                               bf16x8 (&pk)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int cc = 0; cc < NCOL; ++cc) {
-      float psum = 0.0f;
 #pragma unroll
       for (int half = 0; half < SPC / 8; ++half) {
         bf16x8 frag;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float p = __builtin_amdgcn_exp2f(fmaf(SH::get(s, cc, half * 8 + e), cm, mneg[cc]));
-          psum += p;
+          l_run[cc] += p;
           frag[e] = (__bf16)p;
         }
         pk[cc + half] = frag;
       }
-      l_run[cc] += psum;
     }
   };
 
