@@ -273,6 +273,11 @@ bwd_dkdv_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dkT[tb][r] = dvT[tb][r] = 0.0f;
   const float c2 = scale * kLog2e;
+  // the mask's per-lane limit plus the tile's first query q0 (< L): a key
+  // at or past L is dead for every slot (key + 32 - q0 > 31), a causal key
+  // kw0 + col for the queries before it (lanes of half hi hold queries
+  // q0 + 4 hi + ...), otherwise none (0 - q0 <= 0)
+  const int key_lim = kw0 + col >= L ? kw0 + col + 32 : (causal ? kw0 + col - 4 * hi : 0);
 
   if (grp < n_qt) load_qtile(grp, 0);
   for (int i = 0; i < n_iter; ++i) {
@@ -330,7 +335,10 @@ bwd_dkdv_kernel(
     // P = 2^(c2 s - log2e lse), dS = P (dP - D); lane (key col) holds
     // queries 8 (r / 4) + 4 hi + r % 4
     bf16x8 pk[2], dsk[2];
-    const int key = kw0 + col;
+    // masked scores go in as -inf (2^-inf = 0): a select, where a
+    // conditional exponential would become a branch per element.  Slot
+    // r = 4 a + c holds query q0 + 4 hi + (8 a + c), dead when 8 a + c < lim.
+    const int lim = key_lim - q0;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const f32x4 l4 = *reinterpret_cast<const LDS_AS f32x4*>(st + 8 * a + 4 * hi);
@@ -340,12 +348,8 @@ bwd_dkdv_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int r = 4 * a + c;
-        const int qi = q0 + 8 * a + 4 * hi + c;
-        const bool dead = (causal && key > qi) || key >= L;
-        // masked scores go in as -inf (2^-inf = 0): a select, where a
-        // conditional exponential would become a branch per element
         const float x = fmaf(S[r], c2, -lv[c] * kLog2e);
-        const float p = __builtin_amdgcn_exp2f(dead ? -INFINITY : x);
+        const float p = __builtin_amdgcn_exp2f(8 * a + c < lim ? -INFINITY : x);
         const float ds = p * (dP[r] - dv4[c]);
         pk[r >> 3][r & 7] = (__bf16)p;
         dsk[r >> 3][r & 7] = (__bf16)ds;
@@ -570,11 +574,20 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
       // dS^T = P^T (dP^T - D), lane (query col) holds keys 8 (r / 4) + 4 hi + r % 4
       bf16x8 dsk[2];
 #pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] = fmaf(S[r], c2, -lse2);
+      // masked scores go in as -inf (2^-inf = 0), only where some key of the
+      // half lies past some query of the wave or past L (a test uniform over
+      // the wave).  Slot r holds key j0 + 4 hi + (8 (r / 4) + r % 4), dead
+      // past lim: the lane's query (causal) or L - 1, less j0 + 4 hi.
+      if ((causal && j0 + 31 > q0) || j0 + 31 >= L) {
+        const int lim = min(causal ? qi : INT_MAX, L - 1) - j0 - 4 * hi;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) > lim) S[r] = -INFINITY;
+      }
+#pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int j = j0 + (r >> 2) * 8 + hi * 4 + (r & 3);
-        const bool dead = (causal && j > qi) || j >= L;
-        const float x = fmaf(S[r], c2, -lse2);
-        const float p = __builtin_amdgcn_exp2f(dead ? -INFINITY : x);   // 2^-inf = 0
+        const float p = __builtin_amdgcn_exp2f(S[r]);
         dsk[r >> 3][r & 7] = (__bf16)(p * (dP[r] - dlt));
       }
       // dQ^T += K^T dS^T (contraction over the half's keys), MFMA i = (ks,
