@@ -514,7 +514,8 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
       const u32x4 v4 =
           *reinterpret_cast<const LDS_AS u32x4*>(ot + row * OROWB + ((chunk ^ (row & 15)) << 4));
       if (q0 + row < Lq && wave_units > 0)
-        *reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8) = v4;
+        // (non-temporal, as in the bf16 kernel)
+        __builtin_nontemporal_store(v4, reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8));
     }
     if (!has_next) break;
     cur = nx;

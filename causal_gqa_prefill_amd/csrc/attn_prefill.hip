@@ -803,6 +803,11 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
       }
     }
     // read back whole rows: store st covers rows 1024 st / ROWB onwards
+    // (non-temporal stores: the output is not read again here, and the L2
+    // keeps its room for the K/V tiles the XCD's other workgroups still read;
+    // config-2 traffic 1.39 -> 1.25 times the compulsory bytes.  The same
+    // hint on the Q loads made the next item's prologue wait longer, 5%
+    // slower, and saved nothing.)
     unsigned short* obase = out + (((size_t)cur.b * n_q + hb) * Lq64 + (size_t)q0) * D;
 #pragma unroll
     for (int st = 0; st < OT / 1024; ++st) {
@@ -812,7 +817,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
       const u32x4 v4 =
           *reinterpret_cast<const LDS_AS u32x4*>(ot + row * ROWB + ((chunk ^ k_swz<D>(row)) << 4));
       if (q0 + row < Lq && wave_tiles > 0)
-        *reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8) = v4;
+        __builtin_nontemporal_store(v4, reinterpret_cast<u32x4*>(obase + (size_t)row * D + chunk * 8));
     }
     if (!has_next) break;
     cur = nx;
