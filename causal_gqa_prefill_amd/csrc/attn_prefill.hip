@@ -875,10 +875,11 @@ unsigned* dyn_base[kDynMaxDevices] = {};
 std::atomic<unsigned> dyn_next_slot{0};
 
 // rounds of the static schedule before the dynamic tail: all of them when
-// there are fewer than kDynMinRounds (the workgroups of a short schedule
-// finish each round nearly together, so all of them would take a counter
-// entry at once, and those serialised atomics cost more than the balance
-// gains: 3-12% slower at 4 rounds, against 2.4-2.6% faster at 32 and 72);
+// there are fewer than kDynMinRounds (a workgroup draws its next item when
+// it starts the current one, so with a few large items per workgroup the
+// first draws of the tail go to the workgroups that started the previous
+// round first, which the zigzag gave a heavy item there: 3-12% slower at 4
+// rounds, against 2.4-2.6% faster at 32 and 72);
 // otherwise the tail holds the last 30% of the rounds of a causal schedule
 // (about 9% of its work, the heavy-first rounds shrinking towards the end)
 // or the last 10% of a non-causal one
