@@ -85,6 +85,22 @@ def test_chunk_workload_parity(cfg):
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
 
 
+def test_chunk_with_dynamic_tail():
+    """A causal chunk long enough for the schedule's dynamic tail (GQA-8,
+    16384 queries at offset 16384 of 32768 keys: 4096 items, 16 rounds on
+    256 CUs): every output element written (outputs start as NaN), 4096
+    sampled rows against the oracle."""
+    B, Lq, Lk, q_off, n_q, n_kv, d = 1, 16384, 32768, 16384, 64, 8, 128
+    say(f"case chunk with dynamic tail Lq={Lq} Lk={Lk} q_off={q_off} n_q={n_q} n_kv={n_kv}")
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    qb, kb, vb = inputs.make_chunk_qkv(B, Lq, Lk, n_q, n_kv, d, seed=7300)
+    o, l = _run_chunk(qb, kb, vb, q_off, scale, True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l)), "an output row was not written"
+    rows = inputs.sample_rows(B, n_q, Lq, 4096, seed=7300)
+    ref_o, ref_l, _ = oracle.attention_rows_chunk(qb, kb, vb, scale, True, q_offset=q_off, rows=rows)
+    compare("chunk with dynamic tail", o.reshape(-1, d)[rows], l.reshape(-1)[rows], ref_o, ref_l)
+
+
 def test_whole_sequence_chunk_is_bitwise_the_full_entry_point():
     import torch
     from causal_gqa_prefill_amd import attn_prefill, attn_prefill_chunk

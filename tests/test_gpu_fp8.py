@@ -153,6 +153,23 @@ def test_fp8_chunk_workload_parity():
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l)), "an output row was not written"
 
 
+def test_fp8_chunk_with_dynamic_tail():
+    """The FP8 kernel on a causal chunk long enough for the schedule's
+    dynamic tail (GQA-8, 16384 queries at offset 16384 of 32768 keys: 16
+    rounds on 256 CUs): every output element written, 4096 sampled rows
+    within the rounding bound."""
+    B, Lq, Lk, q_off, n_q, n_kv, d = 1, 16384, 32768, 16384, 64, 8, 128
+    say(f"case fp8 chunk with dynamic tail Lq={Lq} Lk={Lk} q_off={q_off}")
+    scale = float(np.float32(d ** -0.5))
+    q8, k8, v8, dq, dk, dv = inputs.make_fp8_qkv(B, Lq, Lk, n_q, n_kv, d, seed=7400)
+    o, l = _run_fp8(q8, k8, v8, dq, dk, dv, scale, 1, q_off)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l)), "an output row was not written"
+    rows = inputs.sample_rows(B, n_q, Lq, 4096, seed=7400)
+    ref_o, ref_l, bound = fp8_reference(q8, k8, v8, scale, dq, dk, dv, 1, q_off, rows)
+    compare_fp8("fp8 chunk with dynamic tail", o.reshape(-1, d)[rows], l.reshape(-1)[rows],
+                ref_o, ref_l, bound)
+
+
 def test_fp8_deterministic_and_errors():
     import torch
     from causal_gqa_prefill_amd import AttnPrefillError, attn_prefill_fp8
