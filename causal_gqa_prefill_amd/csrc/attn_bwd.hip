@@ -283,8 +283,16 @@ bwd_dkdv_kernel(
   for (int i = 0; i < n_iter; ++i) {
     // this wave's loads of tile NG i + grp (and the V rows) have landed;
     // after the barrier every wave's have, and every wave is done with the
-    // buffer the next loads overwrite
+    // buffer the next loads overwrite.  The group's first wave, which loaded
+    // the tile's LSE, turns it into -log2(e) LSE in place before the barrier
+    // (once per tile, instead of a multiply per score in every wave; the
+    // same fp32 product either way)
     wait_vmcnt<0>();
+    if (gw == 0 && NG * i + grp < n_qt) {
+      LDS_AS float* const lse_t = (LDS_AS float*)(gl + G_STOFF + (i & 1) * 512);
+      lse_t[lane] = -(lse_t[lane] * kLog2e);
+      wait_lgkm0();
+    }
     tile_barrier();
     const int n = NG * i + grp;
     if (n + NG < n_qt) load_qtile(n + NG, (i + 1) & 1);
@@ -332,7 +340,8 @@ bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < kKvTrAhead; ++i) load_tr(i);
     __builtin_amdgcn_sched_barrier(0);
-    // P = 2^(c2 s - log2e lse), dS = P (dP - D); lane (key col) holds
+    // P = 2^(c2 s - log2e lse), dS = P (dP - D) (the tile's LSE already
+    // scaled by -log2 e); lane (key col) holds
     // queries 8 (r / 4) + 4 hi + r % 4
     bf16x8 pk[2], dsk[2];
     // masked scores go in as -inf (2^-inf = 0): a select, where a
@@ -348,7 +357,7 @@ bwd_dkdv_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int r = 4 * a + c;
-        const float x = fmaf(S[r], c2, -lv[c] * kLog2e);
+        const float x = fmaf(S[r], c2, lv[c]);   // lv: -log2(e) LSE
         const float p = __builtin_amdgcn_exp2f(8 * a + c < lim ? -INFINITY : x);
         const float ds = p * (dP[r] - dv4[c]);
         pk[r >> 3][r & 7] = (__bf16)p;
