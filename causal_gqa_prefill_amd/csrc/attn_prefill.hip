@@ -1378,22 +1378,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 
 // Key ranges of a decode call.  Two workgroups fill a CU (their LDS), so the
 // workgroups run in rounds of 512 and a call takes about (rounds) x (keys per
-// range + a fixed cost per workgroup).  Ranges are multiples of 256 keys (each of the four waves gets
-// whole 32-key tiles); the count per row is chosen to minimise that product,
-// preferring fewer ranges (less to combine), and never exceeds
-// kDecMaxSplits.
+// range + a fixed cost per workgroup).  Ranges are multiples of 128 keys (each
+// of the four waves gets the same number of whole 32-key tiles); the count per
+// row is chosen to minimise that product, preferring fewer ranges (less to
+// combine), and never exceeds kDecMaxSplits.
 struct DecodeSplit {
   int n_split, split_keys;
 };
 DecodeSplit decode_split(int B, int Lk, int n_kv) {
   const long long pairs = (long long)B * n_kv;
-  const long long chunks = ((long long)Lk + 255) / 256;   // 256-key pieces
+  const long long chunks = ((long long)Lk + 127) / 128;   // 128-key pieces
   const long long max_n = chunks < kDecMaxSplits ? chunks : kDecMaxSplits;
-  long long best_n = 1, best_per = chunks * 256, best_cost = -1;
-  // visit each distinct range length once: q = ceil(chunks / n) 256-key pieces
+  long long best_n = 1, best_per = chunks * 128, best_cost = -1;
+  // visit each distinct range length once: q = ceil(chunks / n) 128-key pieces
   for (long long n = 1; n <= max_n;) {
     const long long q = (chunks + n - 1) / n;
-    const long long per = q * 256;                                // keys per range
+    const long long per = q * 128;                                // keys per range
     const long long n_act = ((long long)Lk + per - 1) / per;      // ranges actually used
     const long long rounds = (pairs * n_act + kDecSlots - 1) / kDecSlots;
     // keys x rounds, with each workgroup's start and merge costing about

@@ -128,12 +128,12 @@ def _ws_splits(B, Lk, n_q, n_kv, d):
                                              (1, 131072, 36, 6, 128), (32, 8192, 32, 8, 128),
                                              (300, 100, 4, 1, 64), (1, 1 << 28, 8, 1, 128)])
 def test_decode_workspace_splits(B, Lk, n_q, n_kv, d):
-    # key ranges of 256-key multiples: at least one, every one non-empty, at
+    # key ranges of 128-key multiples: at least one, every one non-empty, at
     # most 4096 per row
     n = _ws_splits(B, Lk, n_q, n_kv, d)
-    assert 1 <= n <= min(4096, (Lk + 255) // 256)
+    assert 1 <= n <= min(4096, (Lk + 127) // 128)
     per = -(-Lk // n)
-    per = -(-per // 256) * 256
+    per = -(-per // 128) * 128
     assert (n - 1) * per < Lk <= n * per
 
 
