@@ -1104,7 +1104,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
 constexpr int kDecWaves = 4;
 constexpr int kDecTile = 32;          // keys per wave tile
 constexpr int kDecSlots = 512;        // workgroups resident at once (two per CU)
-constexpr int kDecMaxSplits = 4096;   // partials per row the combine stages in LDS
+constexpr int kDecMaxSplits = 4096;   // partials per row (bounds the workspace)
 
 template <int D>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
@@ -1302,77 +1302,89 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
 // decode_combine_kernel: one workgroup of 256 threads per query row merges
 // the row's n_split fp32 partials by their LSEs: M = max lse, w_s =
 // exp(lse_s - M), O = sum w_s o_s / sum w_s (rounded once to bf16),
-// LSE = M + ln sum w_s.
+// LSE = M + ln sum w_s.  Thread (sg, c4) owns four columns of the splits
+// sg, sg + SG, ...; it loads a chunk of kCombChunk of its splits (LSEs and
+// partial outputs together, one memory round trip per chunk) and folds
+// them into a running maximum, weight sum and weighted sum, rescaled when
+// the maximum grows; the SG groups then merge the same way through LDS.
+constexpr int kCombChunk = 16;
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
     unsigned short* __restrict__ out, float* __restrict__ lse, int n_split) {
   constexpr int C4 = D / 4;            // float4 columns of a row
   constexpr int SG = 256 / C4;         // split groups
-  __shared__ float w_s[kDecMaxSplits];
-  __shared__ float red[8];
+  __shared__ float m_g[SG], l_g[SG];
   __shared__ float4 part[SG][C4];
   const int tid = threadIdx.x;
   const size_t row = blockIdx.x;
   const float* lrow = ws_lse + row * n_split;
   const float* orow = ws_o + row * n_split * D;
-
-  // M: strided max, then across the wave (butterfly) and the four waves
-  float m = -INFINITY;
-  for (int s = tid; s < n_split; s += 256) {
-    const float x = lrow[s];
-    w_s[s] = x;
-    m = fmaxf(m, x);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((tid & 63) == 0) red[tid >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  // weights and their sum
-  float wsum = 0.0f;
-  for (int s = tid; s < n_split; s += 256) {
-    const float w = __expf(w_s[s] - m);
-    w_s[s] = w;
-    wsum += w;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
-  if ((tid & 63) == 0) red[4 + (tid >> 6)] = wsum;
-  __syncthreads();
-  wsum = (red[4] + red[5]) + (red[6] + red[7]);
-  // weighted sum of the partial outputs: thread (sg, c4) takes splits sg, sg + SG, ...
   const int c4 = tid % C4;
   const int sg = tid / C4;
+
+  float m = -INFINITY;   // this group's running max of the LSEs
+  float wsum = 0.0f;     // sum of exp(lse_s - m)
   float4 a = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
-  for (int s = sg; s < n_split; s += SG) {
-    const float w = w_s[s];
-    const float4 o = *reinterpret_cast<const float4*>(orow + (size_t)s * D + 4 * c4);
-    a.x += w * o.x;
-    a.y += w * o.y;
-    a.z += w * o.z;
-    a.w += w * o.w;
+  for (int s0 = sg; s0 < n_split; s0 += SG * kCombChunk) {
+    float x[kCombChunk];
+    float4 o[kCombChunk];
+#pragma unroll
+    for (int u = 0; u < kCombChunk; ++u) {
+      const int s = s0 + u * SG;
+      x[u] = -INFINITY;
+      o[u] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (s < n_split) {
+        x[u] = lrow[s];
+        o[u] = *reinterpret_cast<const float4*>(orow + (size_t)s * D + 4 * c4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCombChunk; ++u) {
+      if (s0 + u * SG < n_split) {
+        const float mn = fmaxf(m, x[u]);
+        const float sc = __expf(m - mn);   // 0 for the group's first split
+        const float w = __expf(x[u] - mn);
+        wsum = wsum * sc + w;
+        a.x = a.x * sc + w * o[u].x;
+        a.y = a.y * sc + w * o[u].y;
+        a.z = a.z * sc + w * o[u].z;
+        a.w = a.w * sc + w * o[u].w;
+        m = mn;
+      }
+    }
+  }
+  if (c4 == 0) {
+    m_g[sg] = m;
+    l_g[sg] = wsum;
   }
   part[sg][c4] = a;
   __syncthreads();
   if (tid < C4) {
-    float4 t = part[0][tid];
-    for (int g2 = 1; g2 < SG; ++g2) {
+    float M = m_g[0];   // group 0 holds split 0, so M is finite
+#pragma unroll
+    for (int g2 = 1; g2 < SG; ++g2) M = fmaxf(M, m_g[g2]);
+    float W = 0.0f;
+    float4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int g2 = 0; g2 < SG; ++g2) {
+      if (g2 >= n_split) break;   // groups past the split count hold nothing
+      const float e = __expf(m_g[g2] - M);
       const float4 u = part[g2][tid];
-      t.x += u.x;
-      t.y += u.y;
-      t.z += u.z;
-      t.w += u.w;
+      W += l_g[g2] * e;
+      t.x += u.x * e;
+      t.y += u.y * e;
+      t.z += u.z * e;
+      t.w += u.w * e;
     }
-    const float inv = 1.0f / wsum;
+    const float inv = 1.0f / W;
     bf16x4 y;
     y[0] = (__bf16)(t.x * inv);
     y[1] = (__bf16)(t.y * inv);
     y[2] = (__bf16)(t.z * inv);
     y[3] = (__bf16)(t.w * inv);
     *reinterpret_cast<u32x2*>(out + row * D + 4 * tid) = __builtin_bit_cast(u32x2, y);
-    if (tid == 0) lse[row] = m + __logf(wsum);
+    if (tid == 0) lse[row] = M + __logf(W);
   }
 }
 

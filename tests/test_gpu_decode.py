@@ -63,6 +63,7 @@ DECODES = [
     (3, 4095, 5000, 24, 3, 128),    # g = 8, Lk one short of a tile multiple
     (2, 33, 40, 12, 12, 128),       # MHA decode, Lk just past one tile
     (1, 257, 257, 6, 2, 64),
+    (1, 40000, 40000, 8, 1, 64),    # d_h = 64 with 313 key ranges: two combine chunks
 ]
 
 
