@@ -47,11 +47,6 @@
 #include "attn_prefill.h"
 #include "device_common.h"
 
-// the schedule of a persistent launch: static rounds, then a dynamic tail
-// through the returned counter pair (or none); defined with the bf16 kernels
-unsigned* attn_dyn_tail(long long n_items, long long grid, int causal, hipStream_t stream,
-                        long long* r_static);
-
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -86,7 +81,7 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
     const unsigned char* __restrict__ q, const unsigned char* __restrict__ k,
     const unsigned char* __restrict__ v, unsigned short* __restrict__ out,
     float* __restrict__ lse, int Lq, int Lk, int q_off, int n_q, int n_kv, int n_qblk,
-    int items_per_qblk, int n_items, float c2, float v_mul, int causal, int sg,
+    int items_per_qblk, int n_items, float c2, float v_mul, int causal, int sg, int pair_t,
     unsigned* __restrict__ dyn, int r_static) {
   constexpr int D = kF8D;
   constexpr int BR = kF8Cols / HWG;            // query rows per workgroup
@@ -116,27 +111,23 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
   const int hi = lane >> 5;
   const int col = lane & 31;
 
-  // ---- work items as the bf16 kernel: (b, kv-head, head group, q-block),
-  // heavy q-blocks first; a persistent grid (at most one workgroup per CU)
-  // takes round r's items r G + w (r even) or backwards in blocks of 8 (r
-  // odd), so the workgroups' causal work evens out and each XCD keeps its
-  // (batch, kv-head) streams; or, with sg > 0, the stream blocks of the bf16
-  // kernel (runs of G / 8 consecutive entries of a list cut into super-groups
-  // of sg q-blocks, one run per XCD and round)
+  // ---- work items as the bf16 kernel: (b, kv-head, head group, q-block) in
+  // the list order of ItemList (heavy-first zigzag, stream blocks or
+  // balanced pairs, chosen by the host), then the dynamic tail
   const int g = n_q / n_kv;
   const int ngroups = g / HWG;
   const int c0 = 32 * wave;
   const size_t Lq64 = (size_t)Lq;
+  ItemList lst;
+  lst.n_qblk = n_qblk;
+  lst.ipq = items_per_qblk;
+  lst.ngroups = ngroups;
+  lst.sg = sg;
+  lst.pair_t = pair_t;
+  lst.pair_rounds =
+      pair_t > 0 ? 2 * ((((n_qblk - pair_t) >> 1) * items_per_qblk) / (int)gridDim.x) : 0;
   auto item_at = [&] __device__ (int r) __attribute__((always_inline)) {
-    const int G = gridDim.x;
-    const int w = blockIdx.x;
-    if (sg > 0) {
-      const int pos = (G >> 3) * (w & 7) + (w >> 3);
-      return r * G + ((r & 1) ? G - 1 - pos : pos);
-    }
-    if (!(r & 1)) return r * G + w;
-    if ((G & 7) == 0) return r * G + (G - 8 - (w & ~7)) + (w & 7);
-    return r * G + G - 1 - w;
+    return list_item_at(lst, r, blockIdx.x, gridDim.x);
   };
   struct Geo {
     int b, hh, q0, n_tiles;       // batch, this wave's head and first row, tiles streamed
@@ -146,21 +137,7 @@ __global__ __launch_bounds__(64 * kF8Waves) void attn_fwd_fp8_kernel(
   auto geo = [&] __device__ (int item) __attribute__((always_inline)) {
     Geo e;
     int qb, hg, rest;   // rest: the (batch, kv-head) stream
-    if (sg > 0) {
-      const int span = sg * items_per_qblk;
-      const int k_sg = item / span;
-      const int in_sg = item - k_sg * span;
-      const int per = min(sg, n_qblk - k_sg * sg) * ngroups;
-      rest = in_sg / per;
-      const int in_st = in_sg - rest * per;
-      qb = n_qblk - 1 - (k_sg * sg + in_st / ngroups);
-      hg = in_st % ngroups;
-    } else {
-      qb = n_qblk - 1 - item / items_per_qblk;
-      rest = item % items_per_qblk;
-      hg = rest % ngroups;
-      rest /= ngroups;
-    }
+    list_decode(lst, item, gridDim.x, qb, hg, rest);
     const int kvh = rest % n_kv;
     e.b = rest / n_kv;
     e.hh = kvh * g + hg * HWG + c0 / BR;
@@ -556,28 +533,15 @@ int f8_launch(const void* q, const void* k, const void* v, void* out, float* lse
       n_cu < 1)
     return ATTN_PREFILL_ERR_LAUNCH;
   const long long grid = n_items < n_cu ? n_items : n_cu;
-  // stream blocks, chosen as for the bf16 kernel
-  int sg = 0;
-  if (grid % 8 == 0) {
-    const long long slots = grid / 8;
-    if (slots % n_qblk == 0 && items_per_qblk % (8 * (slots / n_qblk)) == 0 &&
-        (n_items / grid) % 2 == 0)
-      sg = n_qblk;
-    else if (n_items >= 16 * grid) {
-      const long long ng = (n_q / n_kv) / HWG;
-      const long long run = std::min<long long>(n_qblk, std::max<long long>(1, slots / ng));
-      if (n_qblk >= 64 * run) sg = (int)run;
-    }
-  }
-  // the dynamic tail of the bf16 kernel's schedule
-  long long r_static = 0;
-  unsigned* dyn = attn_dyn_tail(n_items, grid, causal, stream, &r_static);
+  // the list form and the dynamic tail, chosen as for the bf16 kernel
+  const ItemPlan plan =
+      attn_item_plan(n_items, items_per_qblk, n_qblk, (n_q / n_kv) / HWG, grid, causal, stream);
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<HWG>), dim3((unsigned)grid), dim3(64 * kF8Waves), 0,
                      stream, static_cast<const unsigned char*>(q),
                      static_cast<const unsigned char*>(k), static_cast<const unsigned char*>(v),
                      static_cast<unsigned short*>(out), lse, Lq, Lk, q_off, n_q, n_kv, n_qblk,
-                     (int)items_per_qblk, (int)n_items, c2, v_mul, causal, sg, dyn,
-                     (int)r_static);
+                     (int)items_per_qblk, (int)n_items, c2, v_mul, causal, plan.sg, plan.pair_t,
+                     plan.dyn, (int)plan.r_static);
   return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
 }
 

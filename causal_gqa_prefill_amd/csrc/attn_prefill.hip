@@ -63,11 +63,13 @@
 //    item's last tiles free, and its Q is loaded while the current output is
 //    written, so an item no longer starts by waiting on HBM.  Where the
 //    numbers fit, each XCD takes runs of adjacent q-blocks of one (batch,
-//    kv-head) stream (stream blocks, see item_at), so its L2 fetches a K/V
-//    tile once for all the workgroups that read it.  A schedule of 16 or
-//    more rounds ends in a dynamic tail: the items of its last, lightest
-//    rounds go to whichever workgroup is free next (a counter per call), so
-//    the XCDs, which do not run equally fast, finish together.
+//    kv-head) stream (stream blocks; for long causal sequences as balanced
+//    pairs of q-blocks, which keep the run's workgroups in step from round
+//    to round; see ItemList), so its L2 fetches a K/V tile once for all the
+//    workgroups that read it.  A schedule of 16 or more rounds ends in a
+//    dynamic tail: the items of its last, lightest rounds go to whichever
+//    workgroup is free next (a counter per call), so the XCDs, which do not
+//    run equally fast, finish together.
 //  * LDS rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads
 //    do not collide on banks (see k_swz / v_swz).
 //  * exp is exp2 with scale*log2(e) folded into one FMA; l and acc are only
@@ -167,8 +169,8 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ out,
     float* __restrict__ lse, int Lq, int Lk, int q_off, int n_q, int n_kv, int n_qblk,
-    int items_per_qblk, int n_items, float scale, int causal, int sg, unsigned* __restrict__ dyn,
-    int r_static) {
+    int items_per_qblk, int n_items, float scale, int causal, int sg, int pair_t,
+    unsigned* __restrict__ dyn, int r_static) {
   using SH = Mfma<D, MS>;
   using Scores = typename SH::Scores;
   using Acc = typename SH::Acc;
@@ -204,45 +206,25 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
   // query row offset (inside the wave's 32) of the lane's column c
   auto col_off = [&] __device__ (int c) __attribute__((always_inline)) { return 16 * c + lcol; };
 
-  // ---- work items: (b, kv-head, head group, q-block), numbered heavy
-  // q-blocks first with neighbouring numbers on different heads.  The grid
-  // is persistent (at most one workgroup per CU) and round r covers items
-  // r G .. r G + G - 1: workgroup w takes item r G + w when r is even and
-  // the round's items backwards when r is odd, a zigzag over the
-  // heavy-first list that evens out the causal work of the workgroups.
-  // When G is a multiple of 8 the backward rounds are taken in blocks of 8
-  // (w = 8 a + x takes r G + 8 (G / 8 - 1 - a) + x), so a workgroup only
-  // sees items congruent to w mod 8: workgroups are dealt to the eight XCDs
-  // in turn, so each XCD keeps working on the same (batch, kv-head) streams
-  // when their count is a multiple of 8, and its L2 keeps serving their K/V.
-  //
-  // Stream blocks (sg > 0, chosen by the host): the list is instead cut into
-  // super-groups of sg q-blocks (heaviest first); inside one, every (batch,
-  // kv-head) stream in turn lists its sg q-blocks (heavy first), each with
-  // its head groups.  Workgroup w = 8 s + x (XCD x, slot s) takes position
-  // (G / 8) x + s of each even round and G - 1 minus that of each odd one,
-  // so an XCD works on a run of G / 8 consecutive list entries: a stream's
-  // adjacent q-blocks, which read the same K/V prefix side by side, and the
-  // XCD's L2 fetches each tile once for all of them.  With sg = n_qblk
-  // (short sequences) a run holds whole heads.
-  //
-  // Dynamic tail (dyn != nullptr, chosen by the host): only rounds
-  // 0 .. r_static - 1 follow item_at; the items from r_static G on go out in
-  // list order, one per draw from the call's counter, to the workgroups as
-  // they become free.
+  // ---- work items: (b, kv-head, head group, q-block) in the list order of
+  // ItemList (heavy-first zigzag, stream blocks or balanced pairs, chosen by
+  // the host).  Dynamic tail (dyn != nullptr, chosen by the host): only
+  // rounds 0 .. r_static - 1 follow the static schedule; the entries from
+  // r_static G on go out in list order, one per draw from the call's
+  // counter, to the workgroups as they become free.
   const int g = n_q / n_kv;
   const int ngroups = g / HWG;
   const size_t Lq64 = (size_t)Lq;
+  ItemList lst;
+  lst.n_qblk = n_qblk;
+  lst.ipq = items_per_qblk;
+  lst.ngroups = ngroups;
+  lst.sg = sg;
+  lst.pair_t = pair_t;
+  lst.pair_rounds =
+      pair_t > 0 ? 2 * ((((n_qblk - pair_t) >> 1) * items_per_qblk) / (int)gridDim.x) : 0;
   auto item_at = [&] __device__ (int r) __attribute__((always_inline)) {
-    const int G = gridDim.x;
-    const int w = blockIdx.x;
-    if (sg > 0) {
-      const int pos = (G >> 3) * (w & 7) + (w >> 3);
-      return r * G + ((r & 1) ? G - 1 - pos : pos);
-    }
-    if (!(r & 1)) return r * G + w;
-    if ((G & 7) == 0) return r * G + (G - 8 - (w & ~7)) + (w & 7);
-    return r * G + G - 1 - w;
+    return list_item_at(lst, r, blockIdx.x, gridDim.x);
   };
   struct Geo {
     int qb, hg, kvh, b, n_tiles;  // n_tiles: K/V tiles the workgroup streams
@@ -252,21 +234,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(
   auto geo = [&] __device__ (int item) __attribute__((always_inline)) {
     Geo e;
     int rest;   // the (batch, kv-head) stream
-    if (sg > 0) {
-      const int span = sg * items_per_qblk;
-      const int k_sg = item / span;
-      const int in_sg = item - k_sg * span;
-      const int per = min(sg, n_qblk - k_sg * sg) * ngroups;
-      rest = in_sg / per;
-      const int in_st = in_sg - rest * per;
-      e.qb = n_qblk - 1 - (k_sg * sg + in_st / ngroups);
-      e.hg = in_st % ngroups;
-    } else {
-      e.qb = n_qblk - 1 - item / items_per_qblk;
-      rest = item % items_per_qblk;
-      e.hg = rest % ngroups;
-      rest /= ngroups;
-    }
+    list_decode(lst, item, gridDim.x, e.qb, e.hg, rest);
     e.kvh = rest % n_kv;
     e.b = rest / n_kv;
     // query row i sits at key position q_off + i; K and V hold Lk rows
@@ -913,20 +881,84 @@ unsigned* dyn_counters(hipStream_t stream) {
   return base + 2 * (dyn_next_slot.fetch_add(1, std::memory_order_relaxed) % kDynSlots);
 }
 
+// Balanced pairs (long causal schedules): the tail cut T, q-blocks 0 .. T - 1
+// being the dynamic tail's share, nearest to 0.3 n_qblk within [0.2, 0.4]
+// n_qblk (the tail then holds (T / n_qblk)^2 of the causal work, about 9%,
+// as the last 30% of the rounds of a heavy-first list do) for which the pairs of
+// q-blocks T .. n_qblk - 1 fill whole rounds: (n_qblk - T) / 2 pairs per
+// item of a q-block, times ipq, a multiple of grid, i.e. (n_qblk - T) / 2 a
+// multiple of m = grid / gcd(ipq, grid).  0 when no such T exists.
+long long pair_cut(long long n_qblk, long long ipq, long long grid) {
+  long long a = ipq, b = grid;
+  while (b != 0) {
+    const long long t = a % b;
+    a = b;
+    b = t;
+  }
+  const long long m = grid / a;
+  const long long lo = std::max(1LL, (n_qblk + 4) / 5);
+  const long long hi = 2 * n_qblk / 5;
+  // T = n_qblk - 2 j m; the j nearest the target and its neighbours
+  const long long j0 = 7 * n_qblk / (20 * m);
+  long long best = 0, best_d = -1;
+  for (long long j = j0 - 1; j <= j0 + 2; ++j) {
+    const long long T = n_qblk - 2 * j * m;
+    if (j < 1 || T < lo || T > hi) continue;
+    const long long d = std::llabs(10 * T - 3 * n_qblk);
+    if (best_d < 0 || d < best_d) {
+      best = T;
+      best_d = d;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
-// The schedule of a persistent launch of n_items items on grid workgroups:
-// *r_static rounds static, then the dynamic tail through the returned
-// counter pair, or (nullptr) every round static.  Shared with the FP8
-// kernel's launch.
-__attribute__((visibility("hidden"))) unsigned* attn_dyn_tail(long long n_items, long long grid,
-                                                              int causal, hipStream_t stream,
-                                                              long long* r_static) {
-  *r_static = static_rounds(n_items, grid, causal);
-  if (*r_static * grid >= n_items) return nullptr;
-  unsigned* dyn = dyn_counters(stream);
-  if (dyn == nullptr) *r_static = (n_items + grid - 1) / grid;
-  return dyn;
+__attribute__((visibility("hidden"))) ItemPlan attn_item_plan(long long n_items, long long ipq,
+                                                              long long n_qblk, long long ngroups,
+                                                              long long grid, int causal,
+                                                              hipStream_t stream) {
+  ItemPlan p{0, 0, 0, nullptr};
+  const long long R = (n_items + grid - 1) / grid;
+  if (grid % 8 == 0) {
+    const long long slots = grid / 8;
+    // short sequences: whole heads per XCD and round when they fill every
+    // round exactly and the rounds pair up (every round then holds heavy and
+    // light q-blocks, and an unpaired last round would leave its heavy ones
+    // running alone)
+    if (slots % n_qblk == 0 && ipq % (8 * (slots / n_qblk)) == 0 && (n_items / grid) % 2 == 0) {
+      p.sg = (int)n_qblk;
+    } else if (n_items >= 16 * grid) {
+      // long sequences: runs of one or two streams per XCD, as balanced
+      // pairs when causal and the pairs fill whole rounds; otherwise plain
+      // stream blocks, whose super-groups do not line up with the rounds, so
+      // only when there are many rounds and many super-groups (each spanning
+      // a small share of the causal weights) does the zigzag still even the
+      // work out (within 0.1% over a sweep of shapes)
+      const long long T = causal ? pair_cut(n_qblk, ipq, grid) : 0;
+      if (T > 0) {
+        p.pair_t = (int)T;
+        p.sg = (int)std::min((n_qblk - T) / 2, std::max(1LL, slots / ngroups));
+      } else {
+        const long long run = std::min(n_qblk, std::max(1LL, slots / ngroups));
+        if (n_qblk >= 64 * run) p.sg = (int)run;
+      }
+    }
+  }
+  if (p.pair_t > 0) {
+    // the pairs' rounds static, q-blocks 0 .. T - 1 the tail
+    const long long pair_rounds = 2 * (((n_qblk - p.pair_t) / 2) * ipq / grid);
+    p.dyn = dyn_counters(stream);
+    p.r_static = p.dyn != nullptr ? pair_rounds : R;
+  } else {
+    p.r_static = static_rounds(n_items, grid, causal);
+    if (p.r_static * grid < n_items) {
+      p.dyn = dyn_counters(stream);
+      if (p.dyn == nullptr) p.r_static = R;
+    }
+  }
+  return p;
 }
 
 namespace {
@@ -953,36 +985,16 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, c
       n_cu < 1)
     return ATTN_PREFILL_ERR_LAUNCH;
   const long long grid = n_items < n_cu ? n_items : n_cu;
-  // stream blocks.  Short sequences: whole heads per XCD and round when
-  // they fill every round exactly and the rounds pair up (every round then
-  // holds heavy and light q-blocks, and an unpaired last round would leave
-  // its heavy ones running alone).
-  int sg = 0;
-  if (grid % 8 == 0) {
-    const long long slots = grid / 8;
-    if (slots % n_qblk == 0 && items_per_qblk % (8 * (slots / n_qblk)) == 0 &&
-        (n_items / grid) % 2 == 0)
-      sg = n_qblk;
-    // long sequences: runs of one or two streams per XCD; the super-groups
-    // do not line up with the rounds, so only when there are many rounds and
-    // many super-groups (each spanning a small share of the causal weights)
-    // does the zigzag still even the work out (within 0.1% over a sweep of
-    // shapes)
-    else if (n_items >= 16 * grid) {
-      const long long ng = (sh.n_q / sh.n_kv) / HWG;
-      const long long run = std::min<long long>(n_qblk, std::max<long long>(1, slots / ng));
-      if (n_qblk >= 64 * run) sg = (int)run;
-    }
-  }
-  // the dynamic tail, when the schedule has one and a counter pair is at hand
-  long long r_static = 0;
-  unsigned* dyn = attn_dyn_tail(n_items, grid, causal, stream, &r_static);
+  // the list form and the dynamic tail
+  const ItemPlan plan = attn_item_plan(n_items, items_per_qblk, n_qblk,
+                                       (sh.n_q / sh.n_kv) / HWG, grid, causal, stream);
   hipLaunchKernelGGL((attn_fwd_kernel<D, HWG, MS>), dim3((unsigned)grid), dim3(kWaves * 64), 0,
                      stream,
                      static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
                      static_cast<const unsigned short*>(v), static_cast<unsigned short*>(out), lse,
                      sh.Lq, sh.Lk, sh.q_off, sh.n_q, sh.n_kv, n_qblk, (int)items_per_qblk,
-                     (int)n_items, scale, causal, sg, dyn, (int)r_static);
+                     (int)n_items, scale, causal, plan.sg, plan.pair_t, plan.dyn,
+                     (int)plan.r_static);
   return hipGetLastError() == hipSuccess ? ATTN_PREFILL_OK : ATTN_PREFILL_ERR_LAUNCH;
 }
 

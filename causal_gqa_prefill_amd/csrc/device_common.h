@@ -1,7 +1,8 @@
 // device_common.h -- small device helpers shared by the attention kernels
-// (gfx950 only): vector types, lane-pair reductions, barriers and waits, and
-// the global -> LDS tile load.  Included by each kernel source; everything
-// here has internal linkage.
+// (gfx950 only): vector types, lane-pair reductions, barriers and waits, the
+// global -> LDS tile load and the forward kernels' work list.  Included by
+// each kernel source; everything here has internal linkage except the host
+// schedule planner declared at the end (defined with the bf16 launch).
 #ifndef ATTN_DEVICE_COMMON_H
 #define ATTN_DEVICE_COMMON_H
 
@@ -122,6 +123,92 @@ __device__ __forceinline__ void dma_tile(const void* base, const int* src, int l
   for (int s = 0; s < loads; ++s) lds_load_b128(rsrc, src[s], dst + s * 1024);
 }
 
+// ---- the forward kernels' work list.  A work item is (batch, kv-head, head
+// group, q-block); the list numbers the items and a persistent grid of G
+// workgroups (at most one per CU) computes them in rounds.  `stream` below
+// is b * n_kv + kv-head, whose K/V rows the item reads.
+//
+// * Default: heavy q-blocks first, neighbouring numbers on different head
+//   groups and streams; round r is items r G .. r G + G - 1, taken forwards
+//   when r is even and backwards when it is odd (in blocks of 8 when G is a
+//   multiple of 8, so that a workgroup only sees items congruent to w mod
+//   8), a zigzag that evens out the workgroups' causal work.  Workgroups are
+//   dealt to the eight XCDs in turn (workgroup w runs on XCD w mod 8).
+// * Stream blocks (sg > 0): the list is cut into super-groups of sg
+//   q-blocks, heaviest first; inside one, every stream in turn lists its sg
+//   q-blocks (heavy first) with their head groups.  Workgroup w = 8 s + x
+//   (XCD x, slot s) takes position (G / 8) x + s of each round, backwards in
+//   odd rounds, so an XCD works on a run of G / 8 consecutive entries:
+//   adjacent q-blocks of one or two streams, which read the same K/V prefix
+//   side by side, so the XCD's L2 fetches each tile once for all of them.
+// * Balanced pairs (pair_t > 0, causal): q-blocks pair_t .. n_qblk - 1 form
+//   the pairs (n_qblk - 1 - i, pair_t + i), whose causal lengths sum to the
+//   same total for every i.  The pairs are listed in stream blocks of sg
+//   values of i; pair round k (rounds 2k and 2k + 1) gives workgroup w the
+//   pair at position k G + (G / 8) x + s, its heavy member in round 2k and
+//   its light member in round 2k + 1.  Every workgroup of an XCD then starts
+//   each even round at the same moment (no drift builds up between rounds),
+//   so the run of adjacent q-blocks on the XCD stays in step and keeps
+//   sharing its L2.  The host makes the pairs fill whole rounds; the items of
+//   q-blocks 0 .. pair_t - 1 follow in the list, heavy first (the dynamic
+//   tail's share; without the tail they run as zigzag rounds).
+struct ItemList {
+  int n_qblk, ipq, ngroups;   // q-blocks; items per q-block (streams x head groups); head groups
+  int sg, pair_t, pair_rounds;
+};
+
+// The list entry workgroup w computes in round r of the static schedule.
+__device__ __forceinline__ int list_item_at(const ItemList& s, int r, int w, int G) {
+  if (s.sg > 0) {
+    const int pos = (G >> 3) * (w & 7) + (w >> 3);
+    if (s.pair_t > 0 && r < s.pair_rounds) return r * G + pos;
+    const int rr = s.pair_t > 0 ? r - s.pair_rounds : r;
+    return r * G + ((rr & 1) ? G - 1 - pos : pos);
+  }
+  if (!(r & 1)) return r * G + w;
+  if ((G & 7) == 0) return r * G + (G - 8 - (w & ~7)) + (w & 7);
+  return r * G + G - 1 - w;
+}
+
+// List entry -> (q-block, head group, stream).
+__device__ __forceinline__ void list_decode(const ItemList& s, int item, int G, int& qb, int& hg,
+                                            int& stream) {
+  if (s.pair_t > 0 && item < s.pair_rounds * G) {
+    const int r = item / G;
+    const int p = (r >> 1) * G + (item - r * G);   // pair index
+    const int half = (s.n_qblk - s.pair_t) >> 1;
+    const int span = s.sg * s.ipq;
+    const int k_sg = p / span;
+    const int in_sg = p - k_sg * span;
+    const int per = min(s.sg, half - k_sg * s.sg) * s.ngroups;
+    stream = in_sg / per;
+    const int in_st = in_sg - stream * per;
+    const int i = k_sg * s.sg + in_st / s.ngroups;
+    hg = in_st % s.ngroups;
+    qb = (r & 1) ? s.pair_t + i : s.n_qblk - 1 - i;
+  } else if (s.pair_t > 0) {
+    const int u = item - s.pair_rounds * G;
+    qb = s.pair_t - 1 - u / s.ipq;
+    const int rest = u % s.ipq;
+    hg = rest % s.ngroups;
+    stream = rest / s.ngroups;
+  } else if (s.sg > 0) {
+    const int span = s.sg * s.ipq;
+    const int k_sg = item / span;
+    const int in_sg = item - k_sg * span;
+    const int per = min(s.sg, s.n_qblk - k_sg * s.sg) * s.ngroups;
+    stream = in_sg / per;
+    const int in_st = in_sg - stream * per;
+    qb = s.n_qblk - 1 - (k_sg * s.sg + in_st / s.ngroups);
+    hg = in_st % s.ngroups;
+  } else {
+    qb = s.n_qblk - 1 - item / s.ipq;
+    const int rest = item % s.ipq;
+    hg = rest % s.ngroups;
+    stream = rest / s.ngroups;
+  }
+}
+
 // Host: do [a, a + an) and [b, b + bn) overlap?
 inline bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -129,5 +216,20 @@ inline bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 }
 
 }  // namespace
+
+// Host: the list form and schedule of a persistent forward launch (defined
+// with the bf16 kernel's launch, shared with the FP8 one): sg and pair_t as
+// ItemList describes them, r_static rounds of the static schedule, then the
+// dynamic tail through the counter pair dyn, or (dyn == nullptr) every round
+// static.
+struct ItemPlan {
+  int sg, pair_t;
+  long long r_static;
+  unsigned* dyn;
+};
+__attribute__((visibility("hidden"))) ItemPlan attn_item_plan(long long n_items, long long ipq,
+                                                              long long n_qblk, long long ngroups,
+                                                              long long grid, int causal,
+                                                              hipStream_t stream);
 
 #endif  // ATTN_DEVICE_COMMON_H
