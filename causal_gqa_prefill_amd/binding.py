@@ -63,6 +63,8 @@ def library():
                                                 ci, ci, ci, ctypes.c_float, vp]
         lib.attn_decode_scratch_bytes.restype = ctypes.c_size_t
         lib.attn_decode_scratch_bytes.argtypes = []
+        lib.attn_prefill_schedule.restype = ci
+        lib.attn_prefill_schedule.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp]
         lib.attn_prefill_strerror.restype = ctypes.c_char_p
         lib.attn_prefill_strerror.argtypes = [ci]
         lib.attn_prefill_version.restype = ci
@@ -93,6 +95,36 @@ def fwd_chunk_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, Lq, Lk, q_offset, n_
         ctypes.c_void_p(out_ptr), ctypes.c_void_p(lse_ptr),
         int(B), int(Lq), int(Lk), int(q_offset), int(n_q), int(n_kv), int(d_h), float(scale),
         int(causal), ctypes.c_void_p(stream_ptr))
+
+
+SCHEDULE_PLAN_KEYS = ("grid", "n_items", "n_qblk", "items_per_qblk", "sg", "pair_t", "pair_rounds",
+                      "r_static")
+
+
+def schedule(B, Lq, Lk, q_offset, n_q, n_kv, d_h, causal, n_cu):
+    """attn_prefill_schedule: the forward launch's work list and static rounds
+    on n_cu compute units (host only).  Returns (plan dict, list [n_items, 3]
+    of (q-block, head group, stream), rounds [R, grid] of list entries, -1
+    past the list)."""
+    import numpy as np
+    lib = library()
+    plan = (ctypes.c_longlong * 8)()
+    args = [int(B), int(Lq), int(Lk), int(q_offset), int(n_q), int(n_kv), int(d_h), int(causal),
+            int(n_cu)]
+    st = lib.attn_prefill_schedule(*args, ctypes.cast(plan, ctypes.c_void_p), None, None)
+    if st != ATTN_PREFILL_OK:
+        raise AttnPrefillError(st, strerror(st))
+    info = dict(zip(SCHEDULE_PLAN_KEYS, (int(x) for x in plan)))
+    n_items, grid = info["n_items"], info["grid"]
+    n_rounds = -(-n_items // grid)
+    lst = np.zeros((n_items, 3), dtype=np.int32)
+    rounds = np.zeros((n_rounds, grid), dtype=np.int32)
+    st = lib.attn_prefill_schedule(*args, ctypes.cast(plan, ctypes.c_void_p),
+                                   lst.ctypes.data_as(ctypes.c_void_p),
+                                   rounds.ctypes.data_as(ctypes.c_void_p))
+    if st != ATTN_PREFILL_OK:
+        raise AttnPrefillError(st, strerror(st))
+    return info, lst, rounds
 
 
 def merge_raw(oa_ptr, la_ptr, ob_ptr, lb_ptr, out_ptr, lo_ptr, rows, d_h, stream_ptr):

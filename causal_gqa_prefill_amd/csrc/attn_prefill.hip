@@ -913,14 +913,17 @@ long long pair_cut(long long n_qblk, long long ipq, long long grid) {
   return best;
 }
 
-}  // namespace
-
-__attribute__((visibility("hidden"))) ItemPlan attn_item_plan(long long n_items, long long ipq,
-                                                              long long n_qblk, long long ngroups,
-                                                              long long grid, int causal,
-                                                              hipStream_t stream) {
-  ItemPlan p{0, 0, 0, nullptr};
-  const long long R = (n_items + grid - 1) / grid;
+// The list form of a persistent forward launch and its static rounds when a
+// counter pair is at hand (no GPU call): sg and pair_t as ItemList describes
+// them; pair_rounds the balanced pairs' rounds; r_static the rounds before
+// the dynamic tail (all of them when there is none).
+struct ListForm {
+  int sg, pair_t;
+  long long pair_rounds, r_static;
+};
+ListForm list_form(long long n_items, long long ipq, long long n_qblk, long long ngroups,
+                   long long grid, int causal) {
+  ListForm f{0, 0, 0, 0};
   if (grid % 8 == 0) {
     const long long slots = grid / 8;
     // short sequences: whole heads per XCD and round when they fill every
@@ -928,7 +931,7 @@ __attribute__((visibility("hidden"))) ItemPlan attn_item_plan(long long n_items,
     // light q-blocks, and an unpaired last round would leave its heavy ones
     // running alone)
     if (slots % n_qblk == 0 && ipq % (8 * (slots / n_qblk)) == 0 && (n_items / grid) % 2 == 0) {
-      p.sg = (int)n_qblk;
+      f.sg = (int)n_qblk;
     } else if (n_items >= 16 * grid) {
       // long sequences: runs of one or two streams per XCD, as balanced
       // pairs when causal and the pairs fill whole rounds; otherwise plain
@@ -938,25 +941,32 @@ __attribute__((visibility("hidden"))) ItemPlan attn_item_plan(long long n_items,
       // work out (within 0.1% over a sweep of shapes)
       const long long T = causal ? pair_cut(n_qblk, ipq, grid) : 0;
       if (T > 0) {
-        p.pair_t = (int)T;
-        p.sg = (int)std::min((n_qblk - T) / 2, std::max(1LL, slots / ngroups));
+        f.pair_t = (int)T;
+        f.sg = (int)std::min((n_qblk - T) / 2, std::max(1LL, slots / ngroups));
+        f.pair_rounds = 2 * (((n_qblk - T) / 2) * ipq / grid);
       } else {
         const long long run = std::min(n_qblk, std::max(1LL, slots / ngroups));
-        if (n_qblk >= 64 * run) p.sg = (int)run;
+        if (n_qblk >= 64 * run) f.sg = (int)run;
       }
     }
   }
-  if (p.pair_t > 0) {
-    // the pairs' rounds static, q-blocks 0 .. T - 1 the tail
-    const long long pair_rounds = 2 * (((n_qblk - p.pair_t) / 2) * ipq / grid);
+  // the pairs' rounds static, q-blocks 0 .. T - 1 the tail; otherwise the
+  // last rounds of the list
+  f.r_static = f.pair_t > 0 ? f.pair_rounds : static_rounds(n_items, grid, causal);
+  return f;
+}
+
+}  // namespace
+
+__attribute__((visibility("hidden"))) ItemPlan attn_item_plan(long long n_items, long long ipq,
+                                                              long long n_qblk, long long ngroups,
+                                                              long long grid, int causal,
+                                                              hipStream_t stream) {
+  const ListForm f = list_form(n_items, ipq, n_qblk, ngroups, grid, causal);
+  ItemPlan p{f.sg, f.pair_t, f.r_static, nullptr};
+  if (p.r_static * grid < n_items) {
     p.dyn = dyn_counters(stream);
-    p.r_static = p.dyn != nullptr ? pair_rounds : R;
-  } else {
-    p.r_static = static_rounds(n_items, grid, causal);
-    if (p.r_static * grid < n_items) {
-      p.dyn = dyn_counters(stream);
-      if (p.dyn == nullptr) p.r_static = R;
-    }
+    if (p.dyn == nullptr) p.r_static = (n_items + grid - 1) / grid;
   }
   return p;
 }
@@ -1451,6 +1461,53 @@ extern "C" int attn_prefill_fwd_chunk(const void* q, const void* k, const void* 
                           causal, stream);
 }
 
+extern "C" int attn_prefill_schedule(int B, int Lq, int Lk, int q_offset, int n_q, int n_kv,
+                                     int d_h, int causal, int n_cu, long long* plan, int* list,
+                                     int* rounds) {
+  if (!plan) return ATTN_PREFILL_ERR_NULL_PTR;
+  if (B < 1 || Lq < 1 || Lk < 1 || n_q < 1 || n_kv < 1 || n_cu < 1)
+    return ATTN_PREFILL_ERR_BAD_SHAPE;
+  if (n_q % n_kv != 0) return ATTN_PREFILL_ERR_BAD_GQA;
+  if (d_h != 64 && d_h != 128) return ATTN_PREFILL_ERR_BAD_HEADDIM;
+  if (causal != 0 && causal != 1) return ATTN_PREFILL_ERR_BAD_CAUSAL;
+  if (q_offset < 0 || (causal && (long long)q_offset + Lq > Lk)) return ATTN_PREFILL_ERR_BAD_OFFSET;
+  const int hwg = pick_hwg(n_q / n_kv);
+  const long long br = kCols / hwg;
+  const long long n_qblk = (Lq + br - 1) / br;
+  const long long ngroups = (n_q / n_kv) / hwg;
+  const long long ipq = (long long)B * n_kv * ngroups;
+  const long long n_items = ipq * n_qblk;
+  if (ipq > INT_MAX || n_items > INT_MAX / 2) return ATTN_PREFILL_ERR_SIZE_OVERFLOW;
+  const long long grid = n_items < n_cu ? n_items : n_cu;
+  const ListForm f = list_form(n_items, ipq, n_qblk, ngroups, grid, causal);
+  const long long R = (n_items + grid - 1) / grid;
+  plan[0] = grid;
+  plan[1] = n_items;
+  plan[2] = n_qblk;
+  plan[3] = ipq;
+  plan[4] = f.sg;
+  plan[5] = f.pair_t;
+  plan[6] = f.pair_rounds;
+  plan[7] = f.r_static < R ? f.r_static : R;
+  ItemList lst;
+  lst.n_qblk = (int)n_qblk;
+  lst.ipq = (int)ipq;
+  lst.ngroups = (int)ngroups;
+  lst.sg = f.sg;
+  lst.pair_t = f.pair_t;
+  lst.pair_rounds = (int)f.pair_rounds;
+  if (list)
+    for (long long e = 0; e < n_items; ++e)
+      list_decode(lst, (int)e, (int)grid, list[3 * e], list[3 * e + 1], list[3 * e + 2]);
+  if (rounds)
+    for (long long r = 0; r < R; ++r)
+      for (long long w = 0; w < grid; ++w) {
+        const int it = list_item_at(lst, (int)r, (int)w, (int)grid);
+        rounds[r * grid + w] = it < n_items ? it : -1;
+      }
+  return ATTN_PREFILL_OK;
+}
+
 extern "C" int attn_merge_partials(const void* o_a, const float* lse_a, const void* o_b,
                                    const float* lse_b, void* out, float* lse_out, long long rows,
                                    int d_h, hipStream_t stream) {
@@ -1663,4 +1720,4 @@ extern "C" const char* attn_prefill_strerror(int status) {
   }
 }
 
-extern "C" int attn_prefill_version(void) { return 300; }
+extern "C" int attn_prefill_version(void) { return 400; }

@@ -158,7 +158,8 @@ struct ItemList {
 };
 
 // The list entry workgroup w computes in round r of the static schedule.
-__device__ __forceinline__ int list_item_at(const ItemList& s, int r, int w, int G) {
+// (Host and device: the host's schedule diagnostic runs the same code.)
+__host__ __device__ __forceinline__ int list_item_at(const ItemList& s, int r, int w, int G) {
   if (s.sg > 0) {
     const int pos = (G >> 3) * (w & 7) + (w >> 3);
     if (s.pair_t > 0 && r < s.pair_rounds) return r * G + pos;
@@ -171,8 +172,8 @@ __device__ __forceinline__ int list_item_at(const ItemList& s, int r, int w, int
 }
 
 // List entry -> (q-block, head group, stream).
-__device__ __forceinline__ void list_decode(const ItemList& s, int item, int G, int& qb, int& hg,
-                                            int& stream) {
+__host__ __device__ __forceinline__ void list_decode(const ItemList& s, int item, int G, int& qb,
+                                                     int& hg, int& stream) {
   if (s.pair_t > 0 && item < s.pair_rounds * G) {
     const int r = item / G;
     const int p = (r >> 1) * G + (item - r * G);   // pair index
@@ -180,7 +181,8 @@ __device__ __forceinline__ void list_decode(const ItemList& s, int item, int G, 
     const int span = s.sg * s.ipq;
     const int k_sg = p / span;
     const int in_sg = p - k_sg * span;
-    const int per = min(s.sg, half - k_sg * s.sg) * s.ngroups;
+    const int left = half - k_sg * s.sg;   // values of i in this super-group
+    const int per = (s.sg < left ? s.sg : left) * s.ngroups;
     stream = in_sg / per;
     const int in_st = in_sg - stream * per;
     const int i = k_sg * s.sg + in_st / s.ngroups;
@@ -196,7 +198,8 @@ __device__ __forceinline__ void list_decode(const ItemList& s, int item, int G, 
     const int span = s.sg * s.ipq;
     const int k_sg = item / span;
     const int in_sg = item - k_sg * span;
-    const int per = min(s.sg, s.n_qblk - k_sg * s.sg) * s.ngroups;
+    const int left = s.n_qblk - k_sg * s.sg;   // q-blocks in this super-group
+    const int per = (s.sg < left ? s.sg : left) * s.ngroups;
     stream = in_sg / per;
     const int in_st = in_sg - stream * per;
     qb = s.n_qblk - 1 - (k_sg * s.sg + in_st / s.ngroups);

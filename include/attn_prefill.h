@@ -272,6 +272,33 @@ int attn_decode_fwd_noalloc(const void *q, const void *k, const void *v, void *o
 /* Bytes of the static scratch attn_decode_fwd_noalloc uses (16 MiB). */
 size_t attn_decode_scratch_bytes(void);
 
+/*
+ * Diagnostic: the work list and static schedule a forward launch
+ * (attn_prefill_fwd / attn_prefill_fwd_chunk, and attn_prefill_fwd_fp8, whose
+ * work items are the same) of this shape would use on n_cu compute units,
+ * computed on the host by the code the kernels run; no GPU call.  A work item
+ * is (batch, kv-head, head group, q-block); the persistent grid computes the
+ * list in rounds, the early ones statically, the rest as a dynamic tail in
+ * list order ("Long-Context Attention Explained", the causal work and its
+ * balance over thread blocks; the scheduling itself is this library's).
+ *   B, Lq, Lk, q_offset, n_q, n_kv, d_h, causal : as for attn_prefill_fwd_chunk
+ *   n_cu    : compute units the grid is sized for (>= 1)
+ *   plan    : host pointer, 8 values written: grid, n_items, n_qblk, items
+ *             per q-block, sg (stream-block run, 0 = none), pair_t (q-blocks
+ *             below it form the tail of a balanced-pair list, 0 = no pairs),
+ *             pair rounds, static rounds before the dynamic tail
+ *   list    : host pointer to 3 * n_items ints or NULL: (q-block, head group,
+ *             stream = b * n_kv + kv-head) of each list entry
+ *   rounds  : host pointer to ceil(n_items / grid) * grid ints or NULL: the
+ *             list entry workgroup w computes in round r of the all-static
+ *             schedule (r * grid + w), -1 past the list
+ * Call with list = rounds = NULL first to size them.  Returns ATTN_PREFILL_OK,
+ * ATTN_PREFILL_ERR_NULL_PTR (plan NULL) or the shape errors of
+ * attn_prefill_fwd_chunk (ATTN_PREFILL_ERR_BAD_SHAPE also for n_cu < 1).
+ */
+int attn_prefill_schedule(int B, int Lq, int Lk, int q_offset, int n_q, int n_kv, int d_h,
+                          int causal, int n_cu, long long *plan, int *list, int *rounds);
+
 /* Static text for a status code (never NULL). */
 const char *attn_prefill_strerror(int status);
 

@@ -25,13 +25,14 @@ def test_library_exports_header_symbols():
     assert names == ["attn_decode_fwd", "attn_decode_fwd_noalloc", "attn_decode_scratch_bytes",
                      "attn_decode_workspace_bytes", "attn_merge_partials",
                      "attn_prefill_bwd", "attn_prefill_fwd", "attn_prefill_fwd_chunk",
-                     "attn_prefill_fwd_fp8", "attn_prefill_strerror", "attn_prefill_version"]
+                     "attn_prefill_fwd_fp8", "attn_prefill_schedule", "attn_prefill_strerror",
+                     "attn_prefill_version"]
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_strerror():
-    assert binding.library().attn_prefill_version() >= 300
+    assert binding.library().attn_prefill_version() >= 400
     for code in range(0, 15):
         assert binding.strerror(code) not in ("", "unknown status")
     assert binding.strerror(99) == "unknown status"
